@@ -1,0 +1,292 @@
+// C ABI of cpattn: argument validation, the ring driver and error reporting.
+// Declarations and the contract of every entry point are in include/cpattn.h.
+#include "cpattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+#define CPATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(CPATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool valid_dtype(int dt) { return dt == CPATTN_BF16 || dt == CPATTN_FP32; }
+size_t dtype_bytes(int dt) { return dt == CPATTN_FP32 ? 4 : 2; }
+
+// Byte ranges [p, p+n) and [q, q+m) intersect (empty ranges never do).
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+    if (p == nullptr || q == nullptr || n == 0 || m == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + m && b < a + n;
+}
+
+// a * b * ... without int64 overflow; false on overflow or a negative factor.
+bool mul_ok(int64_t& acc, int64_t f) {
+    if (f < 0) return false;
+    if (f != 0 && acc > INT64_MAX / f) return false;
+    acc *= f;
+    return true;
+}
+
+constexpr int64_t kMaxBlocks = (int64_t(1) << 31) - 1;
+
+float resolve_scale(float scale, int64_t d) {
+    if (!(scale > 0.f) || std::isinf(scale)) return 1.0f / std::sqrt((float)d);
+    return scale;
+}
+
+struct AttnCheck {
+    size_t q_bytes, kv_bytes, out_bytes, lse_bytes;
+};
+
+// Shared checks of the attention entry points.
+int check_attn(const void* q, const void* k, const void* v, const void* out, const void* lse, int64_t B, int64_t H,
+               int64_t Sq, int64_t Skv, int64_t kv_ld, int64_t d, int in_dt, int out_dt, AttnCheck& c) {
+    if (B < 1 || H < 1) return fail(CPATTN_ERR_SHAPE, "B and H must be >= 1 (got B=%lld H=%lld)", (long long)B, (long long)H);
+    if (Sq < 0 || Skv < 0) return fail(CPATTN_ERR_SHAPE, "sequence lengths must be >= 0 (Sq=%lld Skv=%lld)", (long long)Sq, (long long)Skv);
+    if (kv_ld < Skv) return fail(CPATTN_ERR_SHAPE, "kv_ld (%lld) must be >= Skv (%lld)", (long long)kv_ld, (long long)Skv);
+    if (d != 64 && d != 128) return fail(CPATTN_ERR_SHAPE, "head dim d must be 64 or 128 (got %lld)", (long long)d);
+    if (!valid_dtype(in_dt)) return fail(CPATTN_ERR_DTYPE, "unsupported input dtype %d", in_dt);
+    if (!valid_dtype(out_dt)) return fail(CPATTN_ERR_DTYPE, "unsupported output dtype %d", out_dt);
+    int64_t nq = B;
+    int64_t nkv = B;
+    int64_t nblk = B;
+    if (!mul_ok(nq, H) || !mul_ok(nq, Sq) || !mul_ok(nq, d) || !mul_ok(nq, 4) || !mul_ok(nkv, H) ||
+        !mul_ok(nkv, kv_ld) || !mul_ok(nkv, d) || !mul_ok(nkv, 4) || !mul_ok(nblk, H) || !mul_ok(nblk, (Sq + 127) / 128))
+        return fail(CPATTN_ERR_SHAPE, "tensor sizes overflow");
+    if (nblk > kMaxBlocks) return fail(CPATTN_ERR_SHAPE, "too many query tiles (%lld)", (long long)nblk);
+    if (Skv > INT32_MAX - 64) return fail(CPATTN_ERR_SHAPE, "Skv too large (%lld)", (long long)Skv);
+    c.q_bytes = (size_t)(B * H * Sq * d) * dtype_bytes(in_dt);
+    // the last plane only reaches row Skv: a chunk passed in place ends inside its parent buffer
+    c.kv_bytes = Skv > 0 ? (size_t)(((B * H - 1) * kv_ld + Skv) * d) * dtype_bytes(in_dt) : 0;
+    c.out_bytes = (size_t)(B * H * Sq * d) * dtype_bytes(out_dt);
+    c.lse_bytes = (size_t)(B * H * Sq) * 4;
+    if (Sq > 0) {
+        if (q == nullptr) return fail(CPATTN_ERR_NULL, "q is NULL");
+        if (out == nullptr) return fail(CPATTN_ERR_NULL, "out is NULL");
+        if (lse == nullptr) return fail(CPATTN_ERR_NULL, "lse is NULL");
+    }
+    if (Skv > 0 && Sq > 0) {
+        if (k == nullptr) return fail(CPATTN_ERR_NULL, "k is NULL");
+        if (v == nullptr) return fail(CPATTN_ERR_NULL, "v is NULL");
+    }
+    const void* ins[3] = {q, k, v};
+    const size_t in_sz[3] = {c.q_bytes, c.kv_bytes, c.kv_bytes};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(out, c.out_bytes, ins[i], in_sz[i]) || overlaps(lse, c.lse_bytes, ins[i], in_sz[i]))
+            return fail(CPATTN_ERR_ALIAS, "out/lse overlap an input");
+    }
+    if (overlaps(out, c.out_bytes, lse, c.lse_bytes)) return fail(CPATTN_ERR_ALIAS, "out overlaps lse");
+    return CPATTN_OK;
+}
+
+cpattn::AttnArgs make_args(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
+                           int64_t Sq, int64_t Skv, int64_t kv_ld, int64_t d, float scale, int in_dt, int out_dt) {
+    cpattn::AttnArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse_out = lse;
+    a.acc_in = nullptr;
+    a.lse_in = nullptr;
+    a.n_planes = B * H;
+    a.Sq = Sq;
+    a.Skv = Skv;
+    a.kv_plane = kv_ld * d;
+    a.scale_log2 = resolve_scale(scale, d) * 1.4426950408889634f;
+    a.mode = cpattn::EPI_STORE;
+    a.out_fp32 = out_dt == CPATTN_FP32;
+    a.in_fp32 = in_dt == CPATTN_FP32;
+    a.d = (int)d;
+    return a;
+}
+
+}  // namespace
+
+CPATTN_EXPORT int cpattn_version(void) { return 100; }
+
+CPATTN_EXPORT const char* cpattn_last_error(void) { return g_last_error; }
+
+CPATTN_EXPORT const char* cpattn_status_string(int status) {
+    switch (status) {
+        case CPATTN_OK: return "ok";
+        case CPATTN_ERR_NULL: return "null pointer";
+        case CPATTN_ERR_SHAPE: return "invalid shape";
+        case CPATTN_ERR_DEGREE: return "invalid degree";
+        case CPATTN_ERR_INDIVISIBLE: return "size not divisible by degree";
+        case CPATTN_ERR_CHUNKS: return "invalid chunk lengths";
+        case CPATTN_ERR_DTYPE: return "unsupported dtype";
+        case CPATTN_ERR_WORKSPACE: return "workspace too small";
+        case CPATTN_ERR_ALIAS: return "output overlaps input";
+        case CPATTN_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+CPATTN_EXPORT int cpattn_block_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                   int64_t H, int64_t Sq, int64_t Skv, int64_t kv_ld, int64_t d, float scale,
+                                   int in_dtype, int out_dtype, void* stream) {
+    AttnCheck c;
+    const int st = check_attn(q, k, v, out, lse, B, H, Sq, Skv, kv_ld, d, in_dtype, out_dtype, c);
+    if (st != CPATTN_OK) return st;
+    if (Sq == 0) return CPATTN_OK;
+    cpattn::AttnArgs a = make_args(q, k, v, out, lse, B, H, Sq, Skv, kv_ld, d, scale, in_dtype, out_dtype);
+    const hipError_t e = cpattn::launch_attn_fwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return CPATTN_OK;
+}
+
+CPATTN_EXPORT int cpattn_lse_merge(float* acc_out, float* acc_lse, const void* blk_out, const float* blk_lse,
+                                   int64_t rows, int64_t d, int blk_dtype, void* stream) {
+    if (rows < 0) return fail(CPATTN_ERR_SHAPE, "rows must be >= 0 (got %lld)", (long long)rows);
+    if (d < 4 || d > 256 || (d & (d - 1)) != 0)
+        return fail(CPATTN_ERR_SHAPE, "d must be a power of two in [4, 256] (got %lld)", (long long)d);
+    if (!valid_dtype(blk_dtype)) return fail(CPATTN_ERR_DTYPE, "unsupported partial dtype %d", blk_dtype);
+    if (rows == 0) return CPATTN_OK;
+    if (!acc_out || !acc_lse || !blk_out || !blk_lse) return fail(CPATTN_ERR_NULL, "a merge pointer is NULL");
+    int64_t n = rows;
+    if (!mul_ok(n, d) || !mul_ok(n, 4)) return fail(CPATTN_ERR_SHAPE, "merge size overflows");
+    const size_t acc_b = (size_t)(rows * d) * 4, blk_b = (size_t)(rows * d) * dtype_bytes(blk_dtype);
+    const size_t lse_b = (size_t)rows * 4;
+    if (overlaps(blk_out, blk_b, acc_out, acc_b) || overlaps(blk_out, blk_b, acc_lse, lse_b) ||
+        overlaps(blk_lse, lse_b, acc_out, acc_b) || overlaps(blk_lse, lse_b, acc_lse, lse_b) ||
+        overlaps(acc_out, acc_b, acc_lse, lse_b))
+        return fail(CPATTN_ERR_ALIAS, "merge operands overlap");
+    if ((rows * d / 4 + 1023) / 1024 > kMaxBlocks) return fail(CPATTN_ERR_SHAPE, "merge too large");
+    cpattn::MergeArgs a{acc_out, acc_lse, blk_out, blk_lse, rows, d, blk_dtype == CPATTN_FP32};
+    const hipError_t e = cpattn::launch_lse_merge(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return CPATTN_OK;
+}
+
+CPATTN_EXPORT size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t d, int ring_degree,
+                                                     int out_dtype) {
+    if (B < 1 || H < 1 || Sq < 0 || d < 1 || ring_degree < 1) return 0;
+    if (ring_degree == 1 || out_dtype == CPATTN_FP32) return 0;
+    int64_t n = B;
+    if (!mul_ok(n, H) || !mul_ok(n, Sq) || !mul_ok(n, d) || !mul_ok(n, 4)) return 0;
+    return (size_t)n;
+}
+
+CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                  int64_t H, int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree,
+                                  const int64_t* chunk_lens, void* workspace, size_t workspace_bytes, int in_dtype,
+                                  int out_dtype, void* stream) {
+    if (ring_degree < 1) return fail(CPATTN_ERR_DEGREE, "ring_degree must be >= 1 (got %d)", ring_degree);
+    AttnCheck c;
+    int st = check_attn(q, k, v, out, lse, B, H, Sq, Skv, Skv, d, in_dtype, out_dtype, c);
+    if (st != CPATTN_OK) return st;
+    // chunk geometry (host side, no device sync)
+    if (chunk_lens == nullptr) {
+        if (Skv % ring_degree != 0)
+            return fail(CPATTN_ERR_INDIVISIBLE, "Skv=%lld is not divisible by ring_degree=%d; pass chunk_lens",
+                        (long long)Skv, ring_degree);
+    } else {
+        int64_t sum = 0;
+        for (int i = 0; i < ring_degree; ++i) {
+            if (chunk_lens[i] < 0) return fail(CPATTN_ERR_CHUNKS, "chunk_lens[%d] = %lld < 0", i, (long long)chunk_lens[i]);
+            sum += chunk_lens[i];
+            if (sum > Skv) break;
+        }
+        if (sum != Skv) return fail(CPATTN_ERR_CHUNKS, "chunk lengths do not sum to Skv=%lld", (long long)Skv);
+    }
+    const size_t need = cpattn_ring_fwd_workspace_bytes(B, H, Sq, d, ring_degree, out_dtype);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need)
+            return fail(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+            return fail(CPATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        const void* ins[3] = {q, k, v};
+        const size_t in_sz[3] = {c.q_bytes, c.kv_bytes, c.kv_bytes};
+        for (int i = 0; i < 3; ++i)
+            if (overlaps(workspace, need, ins[i], in_sz[i])) return fail(CPATTN_ERR_ALIAS, "workspace overlaps an input");
+        if (overlaps(workspace, need, out, c.out_bytes) || overlaps(workspace, need, lse, c.lse_bytes))
+            return fail(CPATTN_ERR_ALIAS, "workspace overlaps an output");
+    }
+    if (Sq == 0) return CPATTN_OK;
+
+    // Plan: chunk 0 stores its partial into the fp32 accumulator (the output
+    // itself when it is fp32 or when there is a single chunk), later chunks
+    // LSE-merge into it in their epilogue, and the last one writes `out`.
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t esz = dtype_bytes(in_dtype);
+    const bool acc_is_out = ring_degree == 1 || out_dtype == CPATTN_FP32;
+    float* acc = acc_is_out ? static_cast<float*>(out) : static_cast<float*>(workspace);
+    int64_t off = 0;
+    for (int c_i = 0; c_i < ring_degree; ++c_i) {
+        const int64_t len = chunk_lens ? chunk_lens[c_i] : Skv / ring_degree;
+        const char* kc = static_cast<const char*>(k) + (size_t)off * d * esz;
+        const char* vc = static_cast<const char*>(v) + (size_t)off * d * esz;
+        cpattn::AttnArgs a = make_args(q, kc, vc, nullptr, lse, B, H, Sq, len, Skv, d, scale, in_dtype, out_dtype);
+        const bool last = c_i == ring_degree - 1;
+        if (c_i == 0) {
+            a.mode = cpattn::EPI_STORE;
+        } else {
+            a.mode = cpattn::EPI_MERGE;
+            a.acc_in = acc;
+            a.lse_in = lse;
+        }
+        if (last) {
+            a.out = out;
+            a.out_fp32 = out_dtype == CPATTN_FP32;
+        } else {
+            a.out = acc;
+            a.out_fp32 = 1;
+        }
+        const hipError_t e = cpattn::launch_attn_fwd(a, s);
+        if (e != hipSuccess) return hip_fail(e, "attention kernel launch (ring chunk)");
+        off += len;
+    }
+    return CPATTN_OK;
+}
+
+CPATTN_EXPORT int cpattn_ulysses_permute(const void* in, void* out, int64_t B, int64_t S_local, int64_t H, int64_t d,
+                                         int degree, int group, int direction, int64_t elem_bytes, void* stream) {
+    if (degree < 1) return fail(CPATTN_ERR_DEGREE, "degree must be >= 1 (got %d)", degree);
+    if (group < -1 || group >= degree) return fail(CPATTN_ERR_DEGREE, "group %d outside [-1, %d)", group, degree);
+    if (direction != 0 && direction != 1) return fail(CPATTN_ERR_DTYPE, "direction must be 0 or 1 (got %d)", direction);
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+        return fail(CPATTN_ERR_DTYPE, "elem_bytes must be 1, 2, 4 or 8 (got %lld)", (long long)elem_bytes);
+    if (B < 1 || H < 1 || d < 1 || S_local < 0) return fail(CPATTN_ERR_SHAPE, "invalid permute shape");
+    if (H % degree != 0) return fail(CPATTN_ERR_INDIVISIBLE, "H=%lld is not divisible by degree=%d", (long long)H, degree);
+    int64_t n = degree;
+    if (!mul_ok(n, B) || !mul_ok(n, S_local) || !mul_ok(n, H) || !mul_ok(n, d) || !mul_ok(n, elem_bytes))
+        return fail(CPATTN_ERR_SHAPE, "permute size overflows");
+    const int64_t groups = group < 0 ? degree : 1;
+    const size_t seq_bytes = (size_t)n;                              // [P, B, S_loc, H, d]
+    const size_t head_bytes = (size_t)(n / degree) * (size_t)groups;  // [G, B, H/P, S, d]
+    if (S_local == 0) return CPATTN_OK;
+    if (!in || !out) return fail(CPATTN_ERR_NULL, "in/out is NULL");
+    const size_t in_b = direction == 0 ? seq_bytes : head_bytes;
+    const size_t out_b = direction == 0 ? head_bytes : seq_bytes;
+    if (overlaps(in, in_b, out, out_b)) return fail(CPATTN_ERR_ALIAS, "out overlaps in");
+    int64_t row_bytes = d * elem_bytes;
+    int U = 16;
+    while (U > 1 && row_bytes % U != 0) U >>= 1;
+    if ((B * S_local * (H / degree) * (row_bytes / U)) >= (int64_t(1) << 31))
+        return fail(CPATTN_ERR_SHAPE, "one (rank, group) slice exceeds 2^31 copy units");
+    cpattn::PermuteArgs a{in, out, B, S_local, H, d, degree, group, direction, elem_bytes};
+    const hipError_t e = cpattn::launch_ulysses_permute(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
+    return CPATTN_OK;
+}

@@ -1,0 +1,385 @@
+// Attention forward of one query shard against one K/V block on gfx950.
+//
+// Computes, per (batch, head) plane and query row i,
+//   out_i = sum_j softmax_j(scale * q_i . k_j) v_j,   lse_i = log sum_j exp(scale * q_i . k_j)
+// -- the per-chunk step of ring attention ("Context parallelism" page, Ring
+// Attention; ContextParallelConfig.ring_degree on the "Parallelism" API page)
+// with the unmasked, non-causal scaled_dot_product_attention semantics of the
+// ParaAttention README example.  In EPI_MERGE mode the chunk's (out, lse) is
+// folded into an fp32 accumulator by the log-sum-exp identity in the epilogue
+// (the convert_to_fp32 ring numerics), so the partial never round-trips HBM.
+//
+// Design (one workgroup = 4 waves = 128 query rows of one plane):
+//   * Everything is computed transposed: S^T = K Q^T and O^T = V^T P^T with
+//     v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane then
+//     owns one query column and 16 of every 32 keys, so the row max / row sum
+//     need one cross-half exchange (v_permlane32_swap) and the per-query
+//     rescale of O is lane-local.
+//   * Q stays in VGPRs as MFMA B fragments for the whole kernel.
+//   * K tiles (64 keys) are staged row-major in LDS with a 16-byte row pad;
+//     V tiles are staged transposed (V^T, d-major) with the keys of each
+//     16-key group permuted so that a lane's 8 PV k-slots are one 16-byte read,
+//     and 16-byte units XOR-swizzled by row to keep reads and writes free of
+//     bank conflicts.  Two LDS stages; the next tile's global loads are issued
+//     before the current tile's math and written to LDS after it.
+//   * Softmax in base 2 with scale*log2(e) folded into one FMA per score; the
+//     running max used as the exponent base is only moved when a tile's max
+//     exceeds it by more than 2^8, which keeps the O rescale off the common
+//     path while every exp2 stays <= 256 (exact in the final O/l).
+//   * Workgroup ids are remapped so each XCD (blocks go round-robin over the 8
+//     XCDs) works on a contiguous range of (plane, query-tile) pairs and the
+//     K/V of a plane stays in that XCD's L2.
+#include "internal.h"
+
+#include <math.h>
+
+namespace cpattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 128;  // query rows per workgroup (32 per wave)
+constexpr int BN = 64;   // keys per tile
+constexpr int NT = 256;  // threads per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSlack = 8.0f;  // log2 units a stale exponent base may lag the true max
+
+template <int D>
+struct Cfg {
+    static constexpr int KROW = D * 2 + 16;      // LDS bytes per K row
+    static constexpr int KSTAGE = BN * KROW;
+    static constexpr int VROW = BN * 2;          // LDS bytes per V^T row (64 keys)
+    static constexpr int VSTAGE = D * VROW;
+    static constexpr int STAGE = KSTAGE + VSTAGE;
+    static constexpr int DU = D / 8;             // 16-byte (8 x bf16) units per row
+    static constexpr int KUNITS = BN * DU / NT;  // K units per thread per tile
+    static constexpr int KPT = DU / 4;           // V keys per thread per tile
+    static constexpr int NK = D / 16;            // k-steps of the S^T product
+    static constexpr int NDB = D / 32;           // 32-row blocks of O^T
+    static_assert(KUNITS * NT == BN * DU, "K tile split");
+    static_assert((BN / KPT) * DU == NT, "V tile split");
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value from lane (lane ^ 32) combined with the own value.
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Position of key `k` (0..63) inside a V^T row: bits 2 and 3 of the key's index
+// within its 16-key group are swapped, so the keys {8a + 4h + b} a lane half h
+// feeds to one PV MFMA become 8 consecutive positions.
+__device__ __forceinline__ int vt_pos(int k) {
+    return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
+__device__ __forceinline__ u32x4 cvt8_f32_bf16(f32x4 a, f32x4 b) {
+    f32x8 f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    bf16x8 h = __builtin_convertvector(f, bf16x8);
+    return __builtin_bit_cast(u32x4, h);
+}
+
+// 8 consecutive elements of a row as bf16 bits, from a bf16 or fp32 buffer.
+template <bool F32>
+__device__ __forceinline__ u32x4 load8(const void* base, int64_t elem) {
+    if constexpr (F32) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + elem);
+        return cvt8_f32_bf16(p[0], p[1]);
+    } else {
+        return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
+    }
+}
+
+template <int D, bool F32>
+struct TileRegs {
+    u32x4 k[Cfg<D>::KUNITS];
+    u32x4 v[Cfg<D>::KPT];
+};
+
+// Global -> registers for the tile starting at key t0 (keys >= n are zero).
+template <int D, bool F32>
+__device__ __forceinline__ void load_tile(TileRegs<D, F32>& r, const void* kp, const void* vp, int t0, int n,
+                                          int tid) {
+    using C = Cfg<D>;
+#pragma unroll
+    for (int i = 0; i < C::KUNITS; ++i) {
+        const int u = tid + i * NT;
+        const int row = u / C::DU, c = u % C::DU;
+        const int key = t0 + row;
+        r.k[i] = key < n ? load8<F32>(kp, (int64_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
+    }
+    const int kg = tid / C::DU, dc = tid % C::DU;
+#pragma unroll
+    for (int i = 0; i < C::KPT; ++i) {
+        const int key = t0 + kg * C::KPT + i;
+        r.v[i] = key < n ? load8<F32>(vp, (int64_t)key * D + dc * 8) : u32x4{0, 0, 0, 0};
+    }
+}
+
+// Registers -> LDS stage: K row-major (padded), V transposed + permuted + swizzled.
+template <int D, bool F32>
+__device__ __forceinline__ void store_tile(const TileRegs<D, F32>& r, char* stage, int tid) {
+    using C = Cfg<D>;
+    char* ks = stage;
+    char* vs = stage + C::KSTAGE;
+#pragma unroll
+    for (int i = 0; i < C::KUNITS; ++i) {
+        const int u = tid + i * NT;
+        const int row = u / C::DU, c = u % C::DU;
+        *reinterpret_cast<u32x4*>(ks + row * C::KROW + c * 16) = r.k[i];
+    }
+    const int kg = tid / C::DU, dc = tid % C::DU;
+    const int pos = vt_pos(kg * C::KPT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int d = dc * 8 + j;
+        char* dst = vs + d * C::VROW + (((pos >> 3) ^ vt_swz(d)) << 4) + ((pos & 7) << 1);
+        const int w = j >> 1;
+        if constexpr (C::KPT == 4) {
+            uint32_t lo, hi;
+            if (j & 1) {
+                lo = (r.v[0][w] >> 16) | (r.v[1][w] & 0xFFFF0000u);
+                hi = (r.v[2][w] >> 16) | (r.v[3][w] & 0xFFFF0000u);
+            } else {
+                lo = (r.v[0][w] & 0xFFFFu) | (r.v[1][w] << 16);
+                hi = (r.v[2][w] & 0xFFFFu) | (r.v[3][w] << 16);
+            }
+            *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+        } else {
+            static_assert(C::KPT == 2, "V keys per thread");
+            uint32_t x;
+            if (j & 1)
+                x = (r.v[0][w] >> 16) | (r.v[1][w] & 0xFFFF0000u);
+            else
+                x = (r.v[0][w] & 0xFFFFu) | (r.v[1][w] << 16);
+            *reinterpret_cast<uint32_t*>(dst) = x;
+        }
+    }
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fwd_kernel(AttnArgs a) {
+    using C = Cfg<D>;
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = lane >> 5;   // lane half
+    const int c32 = lane & 31; // query column within the wave's 32
+
+    // XCD-aware mapping of workgroup id -> (plane, query tile).
+    const int nblk = gridDim.x;
+    const int bid = blockIdx.x;
+    const int per = nblk >> 3, rem = nblk & 7;
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int logical = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int nq = (int)((a.Sq + BM - 1) / BM);
+    const int64_t plane = logical / nq;
+    const int qt = logical - (int)plane * nq;
+
+    const int64_t Sq = a.Sq;
+    const int n = (int)a.Skv;
+    const int64_t qrow = (int64_t)qt * BM + wave * 32 + c32;
+    const bool qvalid = qrow < Sq;
+
+    const size_t esz = F32 ? 4 : 2;
+    const char* qp = static_cast<const char*>(a.q) + (size_t)(plane * Sq) * D * esz;
+    const char* kp = static_cast<const char*>(a.k) + (size_t)(plane * a.kv_plane) * esz;
+    const char* vp = static_cast<const char*>(a.v) + (size_t)(plane * a.kv_plane) * esz;
+
+    // Q^T fragments: lane holds q[qrow][16*kk + 8*h .. +7].
+    bf16x8 qf[C::NK];
+#pragma unroll
+    for (int kk = 0; kk < C::NK; ++kk) {
+        u32x4 x = qvalid ? load8<F32>(qp, qrow * D + kk * 16 + h * 8) : u32x4{0, 0, 0, 0};
+        qf[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+
+    f32x16 o[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+
+    float m_run = -INFINITY;  // exponent base (log2 units), identical in lanes l and l^32
+    float l_run = 0.f;        // this lane's share of the row sum
+    const float sl2 = a.scale_log2;
+
+    const int ntiles = (n + BN - 1) / BN;
+    TileRegs<D, F32> regs;
+    if (ntiles > 0) {
+        load_tile<D, F32>(regs, kp, vp, 0, n, tid);
+        store_tile<D, F32>(regs, smem, tid);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        const bool has_next = t + 1 < ntiles;
+        if (has_next) load_tile<D, F32>(regs, kp, vp, (t + 1) * BN, n, tid);
+
+        const char* ks = smem + (t & 1) * C::STAGE;
+        const char* vs = ks + C::KSTAGE;
+
+        // S^T (64 keys x 32 queries) = K_tile . Q^T
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+            const char* krow = ks + (kb * 32 + c32) * C::KROW + h * 16;
+#pragma unroll
+            for (int kk = 0; kk < C::NK; ++kk) {
+                bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + kk * 32);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+            }
+        }
+
+        // Keys past the end of the block never enter the softmax.
+        const int t0 = t * BN;
+        if (t0 + BN > n) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = t0 + kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+                    if (key >= n) s[kb][i] = -INFINITY;
+                }
+        }
+
+        float mt = s[0][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
+        mt = pair_max(mt) * sl2;
+
+        const bool need = mt > m_run + kSlack;
+        float alpha = 1.f;
+        if (need) {
+            alpha = exp2_fast(m_run - mt);
+            m_run = mt;
+        }
+        const float neg_m = -m_run;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = exp2_fast(fmaf(s[kb][i], sl2, neg_m));
+                s[kb][i] = p;
+                rs += p;
+            }
+        l_run = l_run * alpha + rs;
+        if (__any(need)) {
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+
+        // O^T += V^T . P^T, 16 keys per MFMA.
+#pragma unroll
+        for (int ks16 = 0; ks16 < 4; ++ks16) {
+            const int kb = ks16 >> 1, base = (ks16 & 1) * 8;
+            f32x8 pv = {s[kb][base + 0], s[kb][base + 1], s[kb][base + 2], s[kb][base + 3],
+                        s[kb][base + 4], s[kb][base + 5], s[kb][base + 6], s[kb][base + 7]};
+            const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+            const int unit = 2 * ks16 + h;
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                const int d = db * 32 + c32;
+                const bf16x8 vf =
+                    *reinterpret_cast<const bf16x8*>(vs + d * C::VROW + ((unit ^ vt_swz(d)) << 4));
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[db], 0, 0, 0);
+            }
+        }
+
+        if (has_next) store_tile<D, F32>(regs, smem + ((t + 1) & 1) * C::STAGE, tid);
+        __syncthreads();
+    }
+
+    // Epilogue: normalise, then store or LSE-merge into the accumulator.
+    const float l_tot = pair_sum(l_run);
+    const bool any_key = l_tot > 0.f;
+    const float inv_l = any_key ? 1.f / l_tot : 0.f;
+    const float lse2 = any_key ? m_run + log2_fast(l_tot) : -INFINITY;  // log2 units
+    if (!qvalid) return;
+
+    float wa = 0.f, wb = inv_l, lnew2 = lse2;
+    const float* acc = nullptr;
+    if (a.mode == EPI_MERGE) {
+        const float la2 = a.lse_in[plane * Sq + qrow] * kLog2e;
+        const float mx = fmaxf(la2, lse2);
+        if (mx == -INFINITY) {
+            wa = 0.f;
+            wb = 0.f;
+            lnew2 = -INFINITY;
+        } else {
+            const float ea = exp2_fast(la2 - mx);
+            const float eb = exp2_fast(lse2 - mx);
+            const float tot = ea + eb;
+            const float it = 1.f / tot;
+            wa = ea * it;
+            wb = eb * it * inv_l;
+            lnew2 = mx + log2_fast(tot);
+        }
+        acc = a.acc_in + (size_t)(plane * Sq + qrow) * D;
+    }
+
+    const size_t orow = (size_t)(plane * Sq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = db * 32 + g4 * 8 + h * 4;
+            f32x4 r = {o[db][g4 * 4 + 0] * wb, o[db][g4 * 4 + 1] * wb, o[db][g4 * 4 + 2] * wb,
+                       o[db][g4 * 4 + 3] * wb};
+            if (acc != nullptr && wa != 0.f) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(acc + d0);
+                r = r + av * wa;
+            }
+            if (a.out_fp32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + d0) = r;
+            } else {
+                const bf16x4 b = __builtin_convertvector(r, bf16x4);
+                *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + orow + d0) = b;
+            }
+        }
+    if (h == 0) a.lse_out[plane * Sq + qrow] = lnew2 * kLn2;
+}
+
+template <int D, bool F32>
+hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
+    const int64_t nq = (a.Sq + BM - 1) / BM;
+    const int64_t nblk = nq * a.n_planes;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, F32>), dim3((unsigned)nblk), dim3(NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
+    if (a.Sq <= 0 || a.n_planes <= 0) return hipSuccess;
+    if (a.d == 128) return a.in_fp32 ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+    if (a.d == 64) return a.in_fp32 ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace cpattn

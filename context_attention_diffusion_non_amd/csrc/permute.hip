@@ -1,0 +1,137 @@
+// Ulysses sequence <-> head regroup: a strided-to-contiguous row copy.
+//
+// "Context parallelism" page, Ulysses Attention: the all-to-all leaves each
+// rank with every token for a subset of heads; this kernel is the local half of
+// that regroup (and of its inverse), a pure copy of d-element rows:
+//   seq -> head:  out[g'][b][h'][r*S_local + s][:] = in[r][b][s][g*H/P + h'][:]
+//   head -> seq:  the inverse map.
+// Rows are copied in units of U bytes (16 when the row allows); each thread
+// moves UNR units, loads first, then stores.  Index decomposition uses
+// multiply-high division by host-computed magic numbers, so the copy stays
+// memory-bound.  Grid: x over (b, s, h', unit) of one (rank, group) slice,
+// y = rank r, z = group.
+#include "internal.h"
+
+namespace cpattn {
+namespace {
+
+constexpr int NT = 256;
+constexpr int UNR = 4;
+
+// n / d for 0 <= n < 2^31 and 1 <= d < 2^31 (round-up multiplier method):
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    return (__umulhi(n, f.m) + n) >> f.l;
+}
+
+template <int U>
+struct Unit;
+template <> struct Unit<16> { typedef uint4 T; };
+template <> struct Unit<8> { typedef uint2 T; };
+template <> struct Unit<4> { typedef uint32_t T; };
+template <> struct Unit<2> { typedef uint16_t T; };
+template <> struct Unit<1> { typedef uint8_t T; };
+
+struct PermGeom {
+    FastDiv upr;       // units per row
+    FastDiv hp;        // heads per group
+    FastDiv s_loc;     // tokens per shard
+    uint32_t n_units;  // units per (rank, group) slice = B * S_loc * hp * upr
+    int64_t B, S_loc, H, S, hpv, uprv;
+    int g0;            // first group
+    int direction;
+};
+
+template <int U>
+__global__ __launch_bounds__(NT) void permute_kernel(const char* __restrict__ in, char* __restrict__ out,
+                                                     PermGeom g) {
+    typedef typename Unit<U>::T T;
+    const int64_t r = blockIdx.y;       // sequence shard (source rank)
+    const int64_t gi = blockIdx.z;      // group index within this call
+    const int64_t grp = g.g0 + gi;
+    const int64_t P = gridDim.y;
+    // element-row strides, in units
+    const int64_t seq_base = ((r * g.B) * g.S_loc * g.H + grp * g.hpv) * g.uprv;  // in [P,B,S_loc,H,row]
+    const int64_t head_base = (gi * g.B * g.hpv * g.S + r * g.S_loc) * g.uprv;    // in [G,B,hp,S,row]
+    (void)P;
+
+    T val[UNR];
+    int64_t dst[UNR];
+    bool ok[UNR];
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+        const uint32_t x = ((uint32_t)blockIdx.x * UNR + j) * NT + threadIdx.x;
+        ok[j] = x < g.n_units;
+        if (!ok[j]) continue;
+        const uint32_t y = fdiv(x, g.upr);
+        const uint32_t u = x - y * g.upr.d;
+        const uint32_t z = fdiv(y, g.hp);
+        const uint32_t hh = y - z * g.hp.d;
+        const uint32_t b = fdiv(z, g.s_loc);
+        const uint32_t s = z - b * g.s_loc.d;
+        const int64_t seq_idx = seq_base + (((int64_t)b * g.S_loc + s) * g.H + hh) * g.uprv + u;
+        const int64_t head_idx = head_base + (((int64_t)b * g.hpv + hh) * g.S + s) * g.uprv + u;
+        const int64_t src = g.direction == 0 ? seq_idx : head_idx;
+        dst[j] = g.direction == 0 ? head_idx : seq_idx;
+        val[j] = reinterpret_cast<const T*>(in)[src];
+    }
+#pragma unroll
+    for (int j = 0; j < UNR; ++j)
+        if (ok[j]) reinterpret_cast<T*>(out)[dst[j]] = val[j];
+}
+
+template <int U>
+hipError_t launch_u(const PermuteArgs& a, const PermGeom& g, int ngroups, hipStream_t stream) {
+    const uint32_t nblk = (g.n_units + NT * UNR - 1) / (NT * UNR);
+    hipLaunchKernelGGL((permute_kernel<U>), dim3(nblk, (unsigned)a.degree, (unsigned)ngroups), dim3(NT), 0, stream,
+                       static_cast<const char*>(a.in), static_cast<char*>(a.out), g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ulysses_permute(const PermuteArgs& a, hipStream_t stream) {
+    const int64_t row_bytes = a.d * a.elem_bytes;
+    int U = 16;
+    while (U > 1 && row_bytes % U != 0) U >>= 1;
+    const int64_t upr = row_bytes / U;
+    const int64_t hp = a.H / a.degree;
+    const int64_t n_units = a.B * a.S_local * hp * upr;
+    if (n_units <= 0) return hipSuccess;
+    if (n_units >= (int64_t(1) << 31) || upr >= (int64_t(1) << 31) || a.S_local >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+    PermGeom g;
+    g.upr = make_fastdiv((uint32_t)upr);
+    g.hp = make_fastdiv((uint32_t)hp);
+    g.s_loc = make_fastdiv((uint32_t)a.S_local);
+    g.n_units = (uint32_t)n_units;
+    g.B = a.B;
+    g.S_loc = a.S_local;
+    g.H = a.H;
+    g.S = a.S_local * a.degree;
+    g.hpv = hp;
+    g.uprv = upr;
+    g.g0 = a.group < 0 ? 0 : a.group;
+    g.direction = a.direction;
+    const int ngroups = a.group < 0 ? a.degree : 1;
+    switch (U) {
+        case 16: return launch_u<16>(a, g, ngroups, stream);
+        case 8: return launch_u<8>(a, g, ngroups, stream);
+        case 4: return launch_u<4>(a, g, ngroups, stream);
+        case 2: return launch_u<2>(a, g, ngroups, stream);
+        default: return launch_u<1>(a, g, ngroups, stream);
+    }
+}
+
+}  // namespace cpattn

@@ -1,0 +1,150 @@
+"""Python binding of the cpattn C ABI: torch tensors in, library calls out.
+
+Only argument marshalling happens here: torch provides device memory and the
+current HIP stream; every step of the computation runs in the library's
+kernels.  The names mirror the C entry points (cpattn_<name>).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import BF16, FP32, CpattnError, check
+
+_DT = {torch.bfloat16: BF16, torch.float32: FP32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; cpattn takes bfloat16 or float32")
+    return _DT[t.dtype]
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("cpattn tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("cpattn tensors must be contiguous")
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _scale(scale: Optional[float]) -> float:
+    return 0.0 if scale is None else float(scale)
+
+
+def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_len: Optional[int] = None,
+              scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cpattn_block_fwd: attention of q [B,H,Sq,d] against k/v [B,H,kv_ld,d] rows [0, kv_len)."""
+    _dev(q, k, v)
+    B, H, Sq, d = q.shape
+    kv_ld = k.shape[2]
+    skv = kv_ld if kv_len is None else int(kv_len)
+    od = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=od, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _dev(out, lse)
+    check(_lib.lib().cpattn_block_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, skv, kv_ld, d,
+                                      _scale(scale), _dtype_code(q), _dtype_code(out), _stream(q)))
+    return out, lse
+
+
+def lse_merge(acc_out: torch.Tensor, acc_lse: torch.Tensor, blk_out: torch.Tensor, blk_lse: torch.Tensor) -> None:
+    """cpattn_lse_merge: fold (blk_out, blk_lse) into fp32 (acc_out, acc_lse) in place."""
+    _dev(acc_out, acc_lse, blk_out, blk_lse)
+    if acc_out.dtype != torch.float32 or acc_lse.dtype != torch.float32 or blk_lse.dtype != torch.float32:
+        raise TypeError("accumulator and LSE tensors must be float32")
+    d = acc_out.shape[-1]
+    rows = acc_out.numel() // d if d else 0
+    check(_lib.lib().cpattn_lse_merge(_ptr(acc_out), _ptr(acc_lse), _ptr(blk_out), _ptr(blk_lse), rows, d,
+                                      _dtype_code(blk_out), _stream(acc_out)))
+
+
+def ring_fwd_workspace_bytes(B: int, H: int, Sq: int, d: int, ring_degree: int, out_dtype: torch.dtype) -> int:
+    return int(_lib.lib().cpattn_ring_fwd_workspace_bytes(B, H, Sq, d, ring_degree, _DT[out_dtype]))
+
+
+def ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int,
+             chunk_lens: Optional[Sequence[int]] = None, *, scale: Optional[float] = None,
+             out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cpattn_ring_fwd: q [B,H,Sq,d] against k/v [B,H,Skv,d] split into ring_degree chunks."""
+    _dev(q, k, v)
+    B, H, Sq, d = q.shape
+    skv = k.shape[2]
+    od = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, Sq, d), dtype=od, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _dev(out, lse)
+    need = int(_lib.lib().cpattn_ring_fwd_workspace_bytes(B, H, Sq, d, ring_degree, _dtype_code(out)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lens = None
+    if chunk_lens is not None:
+        lens = (ctypes.c_int64 * len(chunk_lens))(*[int(x) for x in chunk_lens])
+        if len(chunk_lens) != ring_degree:
+            raise ValueError("len(chunk_lens) must equal ring_degree")
+    check(_lib.lib().cpattn_ring_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, skv, d,
+                                     _scale(scale), int(ring_degree), lens, _ptr(workspace), ws_bytes,
+                                     _dtype_code(q), _dtype_code(out), _stream(q)))
+    return out, lse
+
+
+def ulysses_permute(x: torch.Tensor, degree: int, group: int = 0, direction: int = 0,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """cpattn_ulysses_permute.
+
+    direction 0: x [P, B, S_local, H, d] -> [B, H/P, P*S_local, d] (group >= 0) or
+                 [P, B, H/P, P*S_local, d] (group == -1).
+    direction 1: x [B, H/P, S, d] (or [P, B, H/P, S, d] for group -1) -> ``out``
+                 [P, B, S/P, H, d], writing only the group's heads (``out`` must be
+                 given, or a zero tensor is created).
+    """
+    _dev(x)
+    eb = x.element_size()
+    if direction == 0:
+        P, B, S_loc, H, d = x.shape
+        if P != degree:
+            raise ValueError("x.shape[0] must equal degree")
+        hp = H // degree if degree > 0 else 0
+        shape = (B, hp, P * S_loc, d) if group >= 0 else (degree, B, hp, P * S_loc, d)
+        if out is None:
+            out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    else:
+        if group >= 0:
+            B, hp, S, d = x.shape
+        else:
+            _, B, hp, S, d = x.shape
+        if degree < 1 or S % degree:
+            raise ValueError("S must divide by degree")
+        S_loc, H = S // degree, hp * degree
+        if out is None:
+            out = torch.zeros((degree, B, S_loc, H, d), dtype=x.dtype, device=x.device)
+    _dev(out)
+    if out.dtype != x.dtype:
+        raise TypeError("out must have x's dtype")
+    check(_lib.lib().cpattn_ulysses_permute(_ptr(x), _ptr(out), B, S_loc, H, d, int(degree), int(group),
+                                            int(direction), eb, _stream(x)))
+    return out
+
+
+__all__ = ["block_fwd", "lse_merge", "ring_fwd", "ring_fwd_workspace_bytes", "ulysses_permute", "CpattnError",
+           "BF16", "FP32"]

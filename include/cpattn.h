@@ -1,0 +1,176 @@
+/*
+ * cpattn -- per-rank attention of ring and Ulysses context parallelism on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The computation is the one a context-parallel rank runs inside its attention
+ * backend: a non-causal, unmasked attention forward of the rank's query shard
+ * against a sequence of key/value chunks, each step producing a partial output
+ * and its log-sum-exp (LSE), the partials merged in fp32 by LSE rescaling, and
+ * the Ulysses sequence<->head regroup as a local permute.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers.  The caller owns all memory;
+ *     the library never allocates or frees device memory.  Scratch space is
+ *     passed in by the caller (cpattn_ring_fwd's workspace).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on it and returns; there is no host<->device
+ *     synchronisation anywhere, and `chunk_lens` is read on the host.
+ *   - Every argument is validated before anything is launched; on any error
+ *     nothing is launched and nothing is written.  The return value is a
+ *     cpattn_status; cpattn_last_error() gives a message for the calling
+ *     thread's most recent failure.
+ *   - Tensors are row-major and contiguous unless a leading dimension is given.
+ *     Attention tensors use the [B, H, S, d] layout (sequence dim -2), the layout
+ *     the ParaAttention README shards with chunk(world_size, dim=-2).
+ *   - LSE values are natural logs of sum_j exp(scale * q.k_j), fp32, [B, H, Sq].
+ *     A row that saw no key has LSE = -inf and output 0.
+ *   - Calls are thread-safe.  Outputs must not overlap inputs except where an
+ *     argument is documented as updated in place.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CPATTN_BF16 = 0, /* bfloat16: attention inputs/outputs */
+    CPATTN_FP32 = 1  /* float32: inputs are rounded to bf16 (nearest-even) when staged for the MFMA path */
+} cpattn_dtype;
+
+typedef enum {
+    CPATTN_OK = 0,
+    CPATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    CPATTN_ERR_SHAPE = 2,       /* a size is out of range (B, H < 1; S < 0; kv_ld < Skv; unsupported d) */
+    CPATTN_ERR_DEGREE = 3,      /* ring or Ulysses degree < 1, or Ulysses group out of range */
+    CPATTN_ERR_INDIVISIBLE = 4, /* sequence or heads do not divide by the degree (no explicit lengths) */
+    CPATTN_ERR_CHUNKS = 5,      /* a chunk length < 0, or the lengths do not sum to Skv */
+    CPATTN_ERR_DTYPE = 6,       /* unsupported dtype / element size / direction */
+    CPATTN_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than required */
+    CPATTN_ERR_ALIAS = 8,       /* an output overlaps an input it must not overlap */
+    CPATTN_ERR_HIP = 9          /* the HIP runtime reported an error; see cpattn_last_error() */
+} cpattn_status;
+
+/*
+ * cpattn_block_fwd -- one chunk step: attention of Q against one K/V block.
+ *
+ * Defines: out = softmax(Q K^T * scale) V and lse = log sum_j exp(scale * q.k_j)
+ * per query row -- the step "each device computes attention between its local
+ * Q and KV chunks" of ring_degree in ContextParallelConfig ("Parallelism" API
+ * page), with the unmasked, non-causal, dropout-free scaled_dot_product_attention
+ * semantics of the ParaAttention README example.
+ *
+ *   q    [B, H, Sq, d]  in_dtype, contiguous.
+ *   k, v planes of Skv rows: plane (b, h) starts at element (b*H + h) * kv_ld * d
+ *        of the buffer, rows [0, Skv) are used, rows are d contiguous elements.
+ *        kv_ld >= Skv lets a chunk of a larger resident K/V buffer be passed in
+ *        place (pointer advanced to the chunk's first row).
+ *   out  [B, H, Sq, d]  out_dtype (CPATTN_FP32 keeps the partial in fp32, the
+ *        convert_to_fp32 ring numerics; CPATTN_BF16 rounds to nearest-even).
+ *   lse  [B, H, Sq]     fp32, natural log.
+ *   d    64 or 128.  scale <= 0 (or NaN) selects 1/sqrt(d).
+ *   Skv == 0 gives out = 0 and lse = -inf.  Sq == 0 is a no-op.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS (out/lse overlapping q/k/v), ERR_HIP.
+ */
+int cpattn_block_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t kv_ld, int64_t d,
+                     float scale, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * cpattn_lse_merge -- fold one partial into an fp32 accumulator by LSE rescaling.
+ *
+ * Defines, per row r (the log-sum-exp identity for attention over two disjoint
+ * key sets; fp32 as convert_to_fp32 asks, "Parallelism" API page):
+ *   L            = log(exp(acc_lse[r]) + exp(blk_lse[r]))
+ *   acc_out[r,:] = exp(acc_lse[r] - L) * acc_out[r,:] + exp(blk_lse[r] - L) * blk_out[r,:]
+ *   acc_lse[r]   = L
+ * A side with LSE = -inf contributes nothing; two such sides give 0 and -inf.
+ *
+ *   acc_out [rows, d] fp32, acc_lse [rows] fp32: updated in place.
+ *   blk_out [rows, d] blk_dtype (CPATTN_FP32, or CPATTN_BF16 for bf16 partials),
+ *   blk_lse [rows] fp32.  rows = B*H*Sq.  d >= 1 with d % 4 == 0.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS (blk overlapping acc), ERR_HIP.
+ */
+int cpattn_lse_merge(float* acc_out, float* acc_lse, const void* blk_out, const float* blk_lse,
+                     int64_t rows, int64_t d, int blk_dtype, void* stream);
+
+/*
+ * Bytes of workspace cpattn_ring_fwd needs for these sizes: an fp32
+ * [B, H, Sq, d] accumulator when ring_degree > 1 and out_dtype is bf16, else 0.
+ * Returns 0 for invalid sizes as well (cpattn_ring_fwd reports those).
+ */
+size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t d, int ring_degree,
+                                       int out_dtype);
+
+/*
+ * cpattn_ring_fwd -- the ring loop of one rank: Q against every K/V chunk in
+ * ring order, each step's (partial out, LSE) merged in fp32 by LSE rescaling.
+ *
+ * Follows the "Context parallelism" page: Ring Attention (each rank attends to
+ * one K/V block per step; after the full loop every rank has seen every token),
+ * Ring Anything Attention (any sequence length: blocks are sliced back to their
+ * true lengths before attention, so padded keys never enter the softmax) and
+ * ContextParallelConfig.convert_to_fp32 (partials and LSE kept in fp32).
+ * K and V are resident for the whole sequence, as the all-gather rotate method
+ * leaves them; chunk c covers rows [off_c, off_c + len_c), off_c = sum of the
+ * earlier lengths.
+ *
+ *   q    [B, H, Sq, d] in_dtype;  k, v [B, H, Skv, d] in_dtype.
+ *   out  [B, H, Sq, d] out_dtype; lse [B, H, Sq] fp32.
+ *   ring_degree >= 1 chunks.  chunk_lens: HOST array of ring_degree lengths, or
+ *   NULL for ring_degree equal chunks (then Skv % ring_degree must be 0, the
+ *   plain Ring Attention requirement).
+ *   workspace: device memory of cpattn_ring_fwd_workspace_bytes(...) bytes,
+ *   256-byte aligned (may be NULL when that is 0).  Its contents are scratch.
+ *   d 64 or 128; scale <= 0 selects 1/sqrt(d).
+ * Result equals attention over all Skv keys up to fp32 rounding of the merges.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_DEGREE, ERR_INDIVISIBLE, ERR_CHUNKS, ERR_DTYPE,
+ *         ERR_WORKSPACE, ERR_ALIAS, ERR_HIP.
+ */
+int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t d, float scale,
+                    int ring_degree, const int64_t* chunk_lens, void* workspace, size_t workspace_bytes,
+                    int in_dtype, int out_dtype, void* stream);
+
+/*
+ * cpattn_ulysses_permute -- the local half of the Ulysses all-to-all.
+ *
+ * "Context parallelism" page, Ulysses Attention: the regroup gives each rank
+ * every token for a subset of the heads; the second regroup returns results by
+ * token.  S and H must divide by the degree P (that page's requirement).
+ *
+ *   direction 0 (sequence -> head):
+ *     in  [P, B, S_local, H, d]: P sequence shards stacked, shard r holding
+ *         tokens [r*S_local, (r+1)*S_local) of all H heads.
+ *     out [B, H/P, P*S_local, d] for head group `group`:
+ *         out[b, h', r*S_local + s, :] = in[r, b, s, group*H/P + h', :]
+ *         group = -1 writes all P groups stacked: [P, B, H/P, P*S_local, d].
+ *   direction 1 (head -> sequence): the inverse map; `in` is the head-sharded
+ *     tensor, `out` the [P, B, S_local, H, d] tensor, of which only the heads of
+ *     the given group(s) are written.
+ *   elem_bytes: 1, 2, 4 or 8 (bf16 = 2).  The copy is bit-exact.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_DEGREE (degree < 1 or group outside [-1, P)),
+ *         ERR_INDIVISIBLE (H % P), ERR_DTYPE (elem_bytes or direction), ERR_ALIAS
+ *         (out overlapping in), ERR_HIP.
+ */
+int cpattn_ulysses_permute(const void* in, void* out, int64_t B, int64_t S_local, int64_t H, int64_t d,
+                           int degree, int group, int direction, int64_t elem_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* cpattn_status_string(int status);
+
+/* Message for the calling thread's most recent failing call ("" if none). */
+const char* cpattn_last_error(void);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int cpattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,0 +1,129 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU.  Every call here
+fails validation (or is pure host code), so nothing is launched."""
+import ctypes
+
+import pytest
+
+from context_attention_diffusion_non_amd import _lib
+
+FAKE = ctypes.c_void_p(0x10000)     # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x20000000)
+FAKE3 = ctypes.c_void_p(0x40000000)
+FAKE4 = ctypes.c_void_p(0x60000000)
+FAKE5 = ctypes.c_void_p(0x70000000)
+NULL = ctypes.c_void_p(0)
+OK, ERR_NULL, ERR_SHAPE, ERR_DEGREE, ERR_INDIV, ERR_CHUNKS, ERR_DTYPE, ERR_WS, ERR_ALIAS = range(9)
+
+
+@pytest.fixture(scope="module")
+def L(lib_path):
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _lib.declared_functions()
+    assert {"cpattn_block_fwd", "cpattn_lse_merge", "cpattn_ring_fwd", "cpattn_ulysses_permute",
+            "cpattn_ring_fwd_workspace_bytes", "cpattn_status_string", "cpattn_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in cpattn.h but not exported"
+
+
+def test_version_and_strings(L):
+    assert L.cpattn_version() >= 100
+    for s in range(10):
+        assert L.cpattn_status_string(s)
+    assert L.cpattn_status_string(99) == b"unknown status"
+
+
+def block(L, q=FAKE, k=FAKE2, v=FAKE3, out=FAKE4, lse=FAKE5, B=1, H=2, Sq=16, Skv=16, ld=16, d=128, idt=0, odt=1):
+    return L.cpattn_block_fwd(q, k, v, out, lse, B, H, Sq, Skv, ld, d, 0.0, idt, odt, NULL)
+
+
+def test_block_fwd_validation(L):
+    assert block(L, B=0) == ERR_SHAPE
+    assert block(L, H=-1) == ERR_SHAPE
+    assert block(L, Sq=-1) == ERR_SHAPE
+    assert block(L, Skv=32, ld=16) == ERR_SHAPE
+    assert block(L, d=96) == ERR_SHAPE
+    assert b"64 or 128" in L.cpattn_last_error()
+    assert block(L, idt=7) == ERR_DTYPE
+    assert block(L, odt=2) == ERR_DTYPE
+    assert block(L, q=NULL) == ERR_NULL
+    assert block(L, k=NULL) == ERR_NULL
+    assert block(L, lse=NULL) == ERR_NULL
+    assert block(L, out=FAKE) == ERR_ALIAS           # out == q
+    assert block(L, lse=FAKE2) == ERR_ALIAS          # lse == k
+    assert block(L, B=1 << 40, H=1 << 40) == ERR_SHAPE
+    # empty query shard is a no-op even with NULL pointers
+    assert block(L, q=NULL, out=NULL, lse=NULL, Sq=0) == OK
+
+
+def ring(L, degree=2, lens=None, Skv=16, ws=NULL, ws_bytes=0, odt=1, B=1, H=2, Sq=16, d=128):
+    arr = None if lens is None else (ctypes.c_int64 * len(lens))(*lens)
+    return L.cpattn_ring_fwd(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, B, H, Sq, Skv, d, 0.0, degree, arr, ws, ws_bytes,
+                             0, odt, NULL)
+
+
+def test_ring_fwd_validation(L):
+    assert ring(L, degree=0) == ERR_DEGREE
+    assert ring(L, degree=-3) == ERR_DEGREE
+    assert ring(L, degree=3, Skv=16) == ERR_INDIV      # plain ring needs S % N == 0
+    assert b"not divisible" in L.cpattn_last_error()
+    assert ring(L, degree=3, lens=[6, 6, 5], Skv=16) == ERR_CHUNKS
+    assert ring(L, degree=3, lens=[6, 11, -1], Skv=16) == ERR_CHUNKS
+    assert ring(L, degree=2, odt=0) == ERR_WS            # bf16 out needs the fp32 accumulator
+    need = L.cpattn_ring_fwd_workspace_bytes(1, 2, 16, 128, 2, 0)
+    assert need == 1 * 2 * 16 * 128 * 4
+    assert ring(L, degree=2, odt=0, ws=ctypes.c_void_p(0x50000000), ws_bytes=need - 1) == ERR_WS
+    assert ring(L, degree=2, odt=0, ws=ctypes.c_void_p(0x50000010), ws_bytes=need) == ERR_WS  # alignment
+    assert ring(L, degree=2, odt=0, ws=FAKE4, ws_bytes=need) == ERR_ALIAS                    # ws == out
+
+
+def test_workspace_bytes(L):
+    f = L.cpattn_ring_fwd_workspace_bytes
+    assert f(1, 24, 2304, 128, 2, 0) == 24 * 2304 * 128 * 4
+    assert f(1, 24, 2304, 128, 1, 0) == 0        # one chunk writes out directly
+    assert f(1, 24, 2304, 128, 4, 1) == 0        # fp32 out doubles as the accumulator
+    assert f(0, 24, 2304, 128, 2, 0) == 0
+
+
+def perm(L, inp=FAKE, out=FAKE2, B=1, S_loc=8, H=4, d=64, P=2, g=0, direction=0, eb=2):
+    return L.cpattn_ulysses_permute(inp, out, B, S_loc, H, d, P, g, direction, eb, NULL)
+
+
+def test_permute_validation(L):
+    assert perm(L, P=0) == ERR_DEGREE
+    assert perm(L, g=2) == ERR_DEGREE
+    assert perm(L, g=-2) == ERR_DEGREE
+    assert perm(L, H=6, P=4) == ERR_INDIV
+    assert perm(L, direction=2) == ERR_DTYPE
+    assert perm(L, eb=3) == ERR_DTYPE
+    assert perm(L, inp=NULL) == ERR_NULL
+    assert perm(L, out=ctypes.c_void_p(0x10000 + 64)) == ERR_ALIAS
+    assert perm(L, S_loc=0) == OK
+
+
+def test_merge_validation(L):
+    m = L.cpattn_lse_merge
+    assert m(FAKE, FAKE2, FAKE3, FAKE4, -1, 128, 1, NULL) == ERR_SHAPE
+    assert m(FAKE, FAKE2, FAKE3, FAKE4, 10, 96, 1, NULL) == ERR_SHAPE
+    assert m(FAKE, FAKE2, FAKE3, FAKE4, 10, 128, 5, NULL) == ERR_DTYPE
+    assert m(FAKE, NULL, FAKE3, FAKE4, 10, 128, 1, NULL) == ERR_NULL
+    assert m(FAKE, FAKE2, FAKE, FAKE4, 10, 128, 1, NULL) == ERR_ALIAS
+    assert m(FAKE, FAKE2, FAKE3, FAKE4, 0, 128, 1, NULL) == OK
+
+
+def test_python_binding_refuses_cpu_tensors(lib_path):
+    import torch
+    from context_attention_diffusion_non_amd import ops
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ops.ring_fwd(q, q, q, 1)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "_HERE", str(tmp_path))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

@@ -1,0 +1,286 @@
+"""GPU parity of the HIP kernels against the fp64 oracle, through the C ABI.
+
+Small and ragged shapes compared element by element, the method's degenerate
+cases, chunked-vs-unsplit, the standalone merge and the bit-exact permute."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from context_attention_diffusion_non_amd import _lib, ops
+from context_attention_diffusion_non_amd import workloads as W
+from tests.gpu_util import (CHUNKED_VS_UNSPLIT, DEV, bits_to_dev, f32_to_dev, log, parity, rand_bf16, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded(lib_path):
+    _lib.lib()
+
+
+def test_tiny_workload_ring():
+    """Tiny ring share: fp32 in/out, Q=256 vs 2 chunks of 128, d=64."""
+    wl = W.WORKLOADS["tiny"]
+    log("[case] tiny ring-2 fp32")
+    x = W.make_inputs(wl)
+    q, k, v = (f32_to_dev(W.to_bhsd(t)) for t in (x.q, x.k, x.v))
+    out, lse = ops.ring_fwd(q, k, v, wl.ring_degree, list(wl.chunk_lens), scale=1 / math.sqrt(64))
+    torch.cuda.synchronize()
+    # the MFMA path consumes bf16-rounded inputs: the graded oracle sees the same values
+    qr, kr, vr = (W.bf16_round(W.to_bhsd(t)).astype(np.float64) for t in (x.q, x.k, x.v))
+    ro, rl = oracle.ring_attention(qr, kr, vr, wl.chunk_lens)
+    parity(out, lse, ro, rl, "tiny vs oracle(bf16-rounded inputs)")
+    raw_o, _ = oracle.ring_attention(W.to_bhsd(x.q), W.to_bhsd(x.k), W.to_bhsd(x.v), wl.chunk_lens)
+    log(f"[info] tiny vs oracle(raw fp32 inputs): max|dout|={np.abs(to_np(out) - raw_o).max():.3e}")
+
+
+SHAPES = [  # B, H, Sq, Skv, d
+    (1, 1, 1, 1, 64), (1, 2, 127, 65, 64), (2, 3, 129, 63, 128), (1, 2, 300, 200, 128),
+    (1, 1, 256, 1000, 128), (1, 1, 33, 777, 64), (1, 4, 128, 64, 128), (3, 1, 257, 129, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
+def test_block_fwd_ragged(shape, out_dtype):
+    B, H, Sq, Skv, d = shape
+    log(f"[case] block_fwd B={B} H={H} Sq={Sq} Skv={Skv} d={d} out={out_dtype}")
+    seed = hash(shape) & 0xFFFF
+    qv, q = rand_bf16(seed, (B, H, Sq, d))
+    kv, k = rand_bf16(seed + 1, (B, H, Skv, d))
+    vv, v = rand_bf16(seed + 2, (B, H, Skv, d))
+    out, lse = ops.block_fwd(q, k, v, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(qv, kv, vv)
+    parity(out, lse, ro, rl, f"block_fwd {shape} {out_dtype}")
+
+
+def test_block_fwd_chunk_window_in_place():
+    """A chunk addressed in place inside a larger resident K/V buffer (kv_ld > Skv)."""
+    B, H, Sq, d, ld, off, n = 2, 3, 70, 128, 300, 50, 123
+    log("[case] block_fwd kv_ld window")
+    qv, q = rand_bf16(11, (B, H, Sq, d))
+    kv, k = rand_bf16(12, (B, H, ld, d))
+    vv, v = rand_bf16(13, (B, H, ld, d))
+    out = torch.empty(B, H, Sq, d, device=DEV)
+    lse = torch.empty(B, H, Sq, device=DEV)
+    st = _lib.lib().cpattn_block_fwd(ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr() + off * d * 2),
+                                     ctypes.c_void_p(v.data_ptr() + off * d * 2), ctypes.c_void_p(out.data_ptr()),
+                                     ctypes.c_void_p(lse.data_ptr()), B, H, Sq, n, ld, d, 0.0, 0, 1,
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    _lib.check(st)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(qv, kv[:, :, off:off + n], vv[:, :, off:off + n])
+    parity(out, lse, ro, rl, "block_fwd kv_ld window")
+
+
+def test_single_key_returns_v():
+    """One key: the softmax weight is 1, so out == v and lse == the score.  The
+    kernel forms the base-2 exponent with one FMA against the rounded scaled
+    max, so the weight is 1 to within the rounding of that product: out == v
+    to 2 ulp (the oracle's pin is exact)."""
+    log("[case] single key")
+    qv, q = rand_bf16(21, (1, 2, 200, 128))
+    kv, k = rand_bf16(22, (1, 2, 1, 128))
+    vv, v = rand_bf16(23, (1, 2, 1, 128))
+    out, lse = ops.block_fwd(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = np.broadcast_to(vv, (1, 2, 200, 128))
+    assert np.all(np.abs(to_np(out) - ref) <= 2.4e-7 * np.abs(ref))
+    s = np.einsum("bhqd,bhkd->bhq", qv, kv) / math.sqrt(128)
+    assert np.abs(to_np(lse) - s).max() < 1e-5
+
+
+def test_zero_query_is_mean_of_v():
+    log("[case] zero query")
+    _, k = rand_bf16(31, (1, 1, 333, 64), scale=3.0)
+    vv, v = rand_bf16(32, (1, 1, 333, 64))
+    q = torch.zeros(1, 1, 70, 64, dtype=torch.bfloat16, device=DEV)
+    out, lse = ops.block_fwd(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.abs(to_np(out) - vv.mean(axis=2, keepdims=True)).max() < 1e-6
+    assert np.abs(to_np(lse) - math.log(333)).max() < 1e-5
+
+
+def test_large_scores_do_not_overflow():
+    """Scores ~ 1e3 after scaling: softmax must stay finite and exact."""
+    log("[case] large scores")
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = 64.0
+    k = torch.zeros(1, 1, 256, 64, dtype=torch.bfloat16, device=DEV)
+    k[..., 0] = torch.linspace(100.0, 140.0, 256, device=DEV).to(torch.bfloat16)
+    vv, v = rand_bf16(41, (1, 1, 256, 64))
+    out, lse = ops.block_fwd(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(to_np(q), to_np(k), vv)
+    parity(out, lse, ro, rl, "large scores")
+
+
+def test_empty_kv():
+    log("[case] empty kv")
+    _, q = rand_bf16(51, (1, 2, 100, 128))
+    k = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device=DEV)
+    out, lse = ops.block_fwd(q, k, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+@pytest.mark.parametrize("lens", [(0, 64, 0, 100), (1, 1, 1, 1, 60), (200, 0), (0, 0, 0), (129, 127, 65, 3)],
+                         ids=str)
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32out", "bf16out"])
+def test_ring_uneven_and_empty_chunks(lens, out_dtype):
+    """Ring Anything style explicit lengths, including empty and length-1 chunks."""
+    log(f"[case] ring lens={lens} out={out_dtype}")
+    skv = sum(lens)
+    qv, q = rand_bf16(61, (2, 2, 150, 128))
+    kv, k = rand_bf16(62, (2, 2, skv, 128))
+    vv, v = rand_bf16(63, (2, 2, skv, 128))
+    out, lse = ops.ring_fwd(q, k, v, len(lens), list(lens), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ring_attention(qv, kv, vv, lens)
+    if skv == 0:
+        assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    else:
+        parity(out, lse, ro, rl, f"ring {lens} {out_dtype}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_ring_chunked_vs_unsplit_and_unfused(d):
+    """GPU chunked (fused merge) vs GPU unsplit, and vs per-chunk block_fwd +
+    standalone lse_merge (the unfused composition), all fp32 out."""
+    log(f"[case] chunked vs unsplit d={d}")
+    lens = [300, 301, 299, 100]
+    qv, q = rand_bf16(71, (1, 3, 333, d))
+    kv, k = rand_bf16(72, (1, 3, sum(lens), d))
+    vv, v = rand_bf16(73, (1, 3, sum(lens), d))
+    ring_o, ring_l = ops.ring_fwd(q, k, v, 4, lens, out_dtype=torch.float32)
+    full_o, full_l = ops.block_fwd(q, k, v, out_dtype=torch.float32)
+    acc_o = torch.empty_like(ring_o)
+    acc_l = torch.full_like(ring_l, -math.inf)
+    acc_o.zero_()
+    off = 0
+    for n in lens:
+        bo, bl = ops.block_fwd(q, k[:, :, off:off + n].contiguous(), v[:, :, off:off + n].contiguous(),
+                               out_dtype=torch.float32)
+        ops.lse_merge(acc_o, acc_l, bo, bl)
+        off += n
+    torch.cuda.synchronize()
+    d1 = (ring_o - full_o).abs().max().item()
+    d2 = (ring_l - full_l).abs().max().item()
+    d3 = (ring_o - acc_o).abs().max().item()
+    d4 = (ring_l - acc_l).abs().max().item()
+    log(f"[parity] chunked-vs-unsplit out={d1:.3e} lse={d2:.3e}; fused-vs-unfused out={d3:.3e} lse={d4:.3e}")
+    assert d1 <= CHUNKED_VS_UNSPLIT and d2 <= CHUNKED_VS_UNSPLIT
+    assert d3 <= 1e-5 and d4 <= 1e-5
+    ro, rl = oracle.ring_attention(qv, kv, vv, lens)
+    parity(acc_o, acc_l, ro, rl, f"unfused ring d={d}")
+
+
+@pytest.mark.parametrize("blk_dtype", [torch.float32, torch.bfloat16], ids=["f32blk", "bf16blk"])
+@pytest.mark.parametrize("d", [64, 128, 4, 256])
+def test_lse_merge_vs_oracle(blk_dtype, d):
+    log(f"[case] lse_merge d={d} blk={blk_dtype}")
+    rows = 3001
+    r = np.random.Generator(np.random.PCG64(d))
+    ao = r.standard_normal((rows, d)).astype(np.float32)
+    bo = r.standard_normal((rows, d)).astype(np.float32)
+    if blk_dtype == torch.bfloat16:
+        bo = W.bf16_round(bo)
+    al = (r.standard_normal(rows) * 4).astype(np.float32)
+    bl = (r.standard_normal(rows) * 4).astype(np.float32)
+    al[::7] = -np.inf
+    bl[::11] = -np.inf
+    ao[::7] = np.nan          # an empty side's values must never reach the result
+    acc_o, acc_l = f32_to_dev(ao), f32_to_dev(al)
+    blk_o = f32_to_dev(bo).to(blk_dtype)
+    blk_l = f32_to_dev(bl)
+    ops.lse_merge(acc_o, acc_l, blk_o, blk_l)
+    torch.cuda.synchronize()
+    ao64 = np.where(np.isnan(ao), 0.0, ao).astype(np.float64)
+    ro, rl = oracle.lse_merge(ao64, al.astype(np.float64), bo.astype(np.float64), bl.astype(np.float64))
+    o, l = to_np(acc_o), to_np(acc_l)
+    assert np.array_equal(np.isneginf(l), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.abs(l[fin] - rl[fin]).max() < 2e-6 * max(1.0, np.abs(rl[fin]).max())
+    assert np.abs(o - ro).max() < 1e-5
+
+
+@pytest.mark.parametrize("P,B,S_loc,H,d,eb", [(2, 1, 8888 // 8, 48, 64, 2), (3, 2, 37, 6, 64, 2),
+                                               (2, 1, 5, 4, 3, 2), (4, 2, 33, 8, 128, 4), (2, 1, 17, 2, 7, 1),
+                                               (1, 2, 9, 3, 64, 2)])
+def test_permute_bit_exact(P, B, S_loc, H, d, eb):
+    log(f"[case] permute P={P} B={B} S_loc={S_loc} H={H} d={d} eb={eb}")
+    r = np.random.Generator(np.random.PCG64(P * 1000 + H))
+    npdt = {1: np.uint8, 2: np.uint16, 4: np.uint32}[eb]
+    tdt = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[eb]
+    x = r.integers(0, np.iinfo(npdt).max, size=(P, B, S_loc, H, d), dtype=npdt)
+    xt = torch.from_numpy(x.view({1: np.uint8, 2: np.int16, 4: np.int32}[eb])).to(DEV)
+    for g in list(range(P)) + [-1]:
+        out = _permute_raw(xt, P, g, 0, tdt, (B, S_loc, H, d))
+        ref = oracle.ulysses_seq_to_head(x, P, g)
+        assert np.array_equal(out.cpu().numpy().view(npdt), ref), f"group {g}"
+        back = torch.full_like(xt, 0)
+        back = _permute_raw(out, P, g, 1, tdt, (B, S_loc, H, d), out=back)
+        ref_back = oracle.ulysses_head_to_seq(ref, P, g, base=np.zeros_like(x))
+        assert np.array_equal(back.cpu().numpy().view(npdt), ref_back), f"inverse group {g}"
+    torch.cuda.synchronize()
+
+
+def _permute_raw(x, P, g, direction, tdt, dims, out=None):
+    B, S_loc, H, d = dims
+    hp = H // P
+    if direction == 0:
+        shape = (B, hp, P * S_loc, d) if g >= 0 else (P, B, hp, P * S_loc, d)
+        out = torch.empty(shape, dtype=tdt, device=DEV)
+    st = _lib.lib().cpattn_ulysses_permute(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, S_loc,
+                                           H, d, P, g, direction, x.element_size(),
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    _lib.check(st)
+    return out
+
+
+def test_ring_is_deterministic():
+    log("[case] determinism")
+    _, q = rand_bf16(81, (1, 4, 500, 128))
+    _, k = rand_bf16(82, (1, 4, 1000, 128))
+    _, v = rand_bf16(83, (1, 4, 1000, 128))
+    a = ops.ring_fwd(q, k, v, 2)
+    b = ops.ring_fwd(q, k, v, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+def test_outputs_stay_in_bounds():
+    """Outputs carved out of a NaN-filled buffer: every byte outside them is untouched."""
+    log("[case] guard bands")
+    B, H, Sq, d = 1, 3, 131, 128
+    _, q = rand_bf16(91, (B, H, Sq, d))
+    _, k = rand_bf16(92, (B, H, 257, d))
+    _, v = rand_bf16(93, (B, H, 257, d))
+    pad = 4096
+    n_out = B * H * Sq * d
+    big = torch.full((pad + n_out + pad,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    big_l = torch.full((pad + B * H * Sq + pad,), float("nan"), dtype=torch.float32, device=DEV)
+    out = big[pad:pad + n_out].view(B, H, Sq, d)
+    lse = big_l[pad:pad + B * H * Sq].view(B, H, Sq)
+    ops.ring_fwd(q, k, v, 3, [100, 100, 57], out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(big[:pad].float()).all() and torch.isnan(big[pad + n_out:].float()).all()
+    assert torch.isnan(big_l[:pad]).all() and torch.isnan(big_l[pad + B * H * Sq:]).all()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+
+
+def test_error_path_launches_nothing():
+    """A failing call writes nothing."""
+    _, q = rand_bf16(95, (1, 1, 64, 128))
+    out = torch.full((1, 1, 64, 128), 7.0, device=DEV)
+    lse = torch.full((1, 1, 64), 7.0, device=DEV)
+    with pytest.raises(_lib.CpattnError) as e:
+        ops.ring_fwd(q, q.clone(), q.clone(), 3, out=out, lse=lse)
+    assert e.value.name == "CPATTN_ERR_INDIVISIBLE"
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(lse == 7.0)

@@ -1,0 +1,82 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (ring_fwd, bf16 in, bf16 out, fp32 merge).
+
+FLUX and Ring-Anything shares are compared in full; the Mochi and CogVideoX
+shares on a deterministic query-row sample (all heads; first/last 64 rows,
+both sides of the 128/256 tile boundaries, 256 seeded random rows) that the
+oracle computes row by row.  The CogVideoX permute is compared bit for bit on
+the whole tensors."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from context_attention_diffusion_non_amd import _lib, ops
+from context_attention_diffusion_non_amd import workloads as W
+from tests.gpu_util import CHUNKED_VS_UNSPLIT, bits_to_dev, log, parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded(lib_path):
+    _lib.lib()
+
+
+def _share(wl, x):
+    qs = slice(wl.q_start, wl.q_start + wl.q_len)
+    q_bits = W.to_bhsd(x.q_bits[:, qs])
+    k_bits, v_bits = W.to_bhsd(x.k_bits), W.to_bhsd(x.v_bits)
+    return q_bits, k_bits, v_bits
+
+
+def _vals(bits):
+    return W.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["flux", "ring_anything", "mochi"])
+def test_ring_workload(name):
+    wl = W.WORKLOADS[name]
+    log(f"[case] workload {name}: B={wl.B} H={wl.H} Sq={wl.q_len} Skv={wl.S} d={wl.d} chunks={wl.chunk_lens}")
+    x = W.make_inputs(wl)
+    qb, kb, vb = _share(wl, x)
+    q, k, v = bits_to_dev(qb), bits_to_dev(kb), bits_to_dev(vb)
+    out, lse = ops.ring_fwd(q, k, v, wl.ring_degree, list(wl.chunk_lens), out_dtype=torch.bfloat16)
+    # chunked vs unsplit on the GPU, both fp32 out
+    ring32, lse32 = ops.ring_fwd(q, k, v, wl.ring_degree, list(wl.chunk_lens), out_dtype=torch.float32)
+    full32, flse32 = ops.block_fwd(q, k, v, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    d_o = (ring32 - full32).abs().max().item()
+    d_l = (lse32 - flse32).abs().max().item()
+    log(f"[parity] {name} chunked-vs-unsplit fp32: out={d_o:.3e} lse={d_l:.3e}")
+    assert d_o <= CHUNKED_VS_UNSPLIT and d_l <= CHUNKED_VS_UNSPLIT
+    if wl.q_len * wl.S * wl.H * wl.B <= 24 * 2304 * 4608:
+        rows = np.arange(wl.q_len)
+    else:
+        rows = W.sample_rows(wl.q_len, seed=wl.seed)
+    ro, rl = oracle.attention_rows(_vals(qb), _vals(kb), _vals(vb), rows)
+    parity(out[:, :, torch.from_numpy(rows).to(out.device)], lse[:, :, torch.from_numpy(rows).to(out.device)],
+           ro, rl, f"{name} ring_fwd bf16 ({len(rows)} rows x {wl.B * wl.H} planes)")
+
+
+def test_cogvideox_ulysses_share():
+    wl = W.WORKLOADS["cogvideox"]
+    P, g = wl.ulysses_degree, wl.ulysses_group
+    S_loc = wl.S // P
+    log(f"[case] workload cogvideox: permute [{P}x{S_loc},{wl.H},{wl.d}] group {g}, then attention")
+    x = W.make_inputs(wl)
+    shards = {n: np.ascontiguousarray(b.reshape(wl.B, P, S_loc, wl.H, wl.d).transpose(1, 0, 2, 3, 4))
+              for n, b in (("q", x.q_bits), ("k", x.k_bits), ("v", x.v_bits))}
+    dev = {n: bits_to_dev(s) for n, s in shards.items()}
+    head = {n: ops.ulysses_permute(t, P, g, 0) for n, t in dev.items()}
+    out, lse = ops.ring_fwd(head["q"], head["k"], head["v"], 1, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref_head = {n: oracle.ulysses_seq_to_head(s, P, g) for n, s in shards.items()}
+    for n in ("q", "k", "v"):
+        got = head[n].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, ref_head[n]), f"permute of {n} not bit-exact"
+    log("[parity] cogvideox permute q/k/v: bit-exact")
+    rows = W.sample_rows(wl.S, seed=wl.seed)
+    ro, rl = oracle.attention_rows(_vals(ref_head["q"]), _vals(ref_head["k"]), _vals(ref_head["v"]), rows)
+    idx = torch.from_numpy(rows).to(out.device)
+    parity(out[:, :, idx], lse[:, :, idx], ro, rl, f"cogvideox attention ({len(rows)} rows x {wl.heads_local} heads)")
