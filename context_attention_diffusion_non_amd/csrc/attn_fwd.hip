@@ -16,12 +16,11 @@
 //     need one cross-half exchange (v_permlane32_swap) and the per-query
 //     rescale of O is lane-local.
 //   * Q stays in VGPRs as MFMA B fragments for the whole kernel.
-//   * K tiles (64 keys) are staged row-major in LDS with a 16-byte row pad;
-//     V tiles are staged transposed (V^T, d-major) with the keys of each
-//     16-key group permuted so that a lane's 8 PV k-slots are one 16-byte read,
-//     and 16-byte units XOR-swizzled by row to keep reads and writes free of
-//     bank conflicts.  Two LDS stages; the next tile's global loads are issued
-//     before the current tile's math and written to LDS after it.
+//   * K and V tiles (64 keys) go global -> LDS directly (LDS DMA), row-major
+//     with an XOR swizzle of 16-byte units per row.  K fragments are plain
+//     16-byte LDS reads; V^T fragments come from two transposing LDS reads
+//     (ds_read_b64_tr_b16), so no register staging or VALU transposes.  Two
+//     LDS stages: the next tile's DMA runs under the current tile's math.
 //   * Softmax in base 2 with scale*log2(e) folded into one FMA per score; the
 //     running max used as the exponent base is only moved when a tile's max
 //     exceeds it by more than 2^8, which keeps the O rescale off the common
@@ -42,7 +41,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr int BM = 128;  // query rows per workgroup (32 per wave)
 constexpr int BN = 64;   // keys per tile
@@ -53,19 +54,29 @@ constexpr float kSlack = 8.0f;  // log2 units a stale exponent base may lag the 
 
 template <int D>
 struct Cfg {
-    static constexpr int KROW = D * 2 + 16;      // LDS bytes per K row
-    static constexpr int KSTAGE = BN * KROW;
-    static constexpr int VROW = BN * 2;          // LDS bytes per V^T row (64 keys)
-    static constexpr int VSTAGE = D * VROW;
-    static constexpr int STAGE = KSTAGE + VSTAGE;
-    static constexpr int DU = D / 8;             // 16-byte (8 x bf16) units per row
-    static constexpr int KUNITS = BN * DU / NT;  // K units per thread per tile
-    static constexpr int KPT = DU / 4;           // V keys per thread per tile
-    static constexpr int NK = D / 16;            // k-steps of the S^T product
-    static constexpr int NDB = D / 32;           // 32-row blocks of O^T
-    static_assert(KUNITS * NT == BN * DU, "K tile split");
-    static_assert((BN / KPT) * DU == NT, "V tile split");
+    static constexpr int RB = D * 2;            // LDS bytes per K or V row (bf16)
+    static constexpr int UPR = D / 8;           // 16-byte units per row
+    static constexpr int TILE = BN * RB;        // bytes of one K (or V) tile
+    static constexpr int STAGE = 2 * TILE;      // K tile + V tile
+    static constexpr int CHUNKS = TILE / 1024;  // 1 KB DMA chunks per tile
+    static constexpr int CPW = CHUNKS / 4;      // chunks per wave
+    static constexpr int NK = D / 16;           // k-steps of the S^T product
+    static constexpr int NDB = D / 32;          // 32-row blocks of O^T
+    static_assert(CHUNKS % 4 == 0, "tile split over 4 waves");
 };
+
+// XOR swizzles of the 16-byte units of a row (rows are unpadded).
+// K: a 16-byte read of 16 consecutive rows at one logical unit hits 16 distinct
+//    bank groups.  V: a transposing 8-byte read over 4 rows x 64 bytes (half a
+//    wave) hits distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_unit(int row, int u) {
+    return D == 128 ? (u ^ (row & 15)) : (u ^ ((row >> 1) & 7));
+}
+template <int D>
+__device__ __forceinline__ int v_unit(int row, int u) {
+    return D == 128 ? (u ^ ((row & 3) << 2)) : (u ^ (((row >> 1) & 1) << 2));
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
@@ -79,14 +90,6 @@ __device__ __forceinline__ float pair_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-// Position of key `k` (0..63) inside a V^T row: bits 2 and 3 of the key's index
-// within its 16-key group are swapped, so the keys {8a + 4h + b} a lane half h
-// feeds to one PV MFMA become 8 consecutive positions.
-__device__ __forceinline__ int vt_pos(int k) {
-    return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 __device__ __forceinline__ u32x4 cvt8_f32_bf16(f32x4 a, f32x4 b) {
     f32x8 f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -105,69 +108,28 @@ __device__ __forceinline__ u32x4 load8(const void* base, int64_t elem) {
     }
 }
 
-template <int D, bool F32>
-struct TileRegs {
-    u32x4 k[Cfg<D>::KUNITS];
-    u32x4 v[Cfg<D>::KPT];
-};
-
-// Global -> registers for the tile starting at key t0 (keys >= n are zero).
-template <int D, bool F32>
-__device__ __forceinline__ void load_tile(TileRegs<D, F32>& r, const void* kp, const void* vp, int t0, int n,
-                                          int tid) {
+// Stage one K or V tile (keys t0 .. t0+63) into LDS.  bf16 sources go
+// global -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes
+// bytes [16 l, 16 l + 16) of the wave's 1 KB chunk); each lane fetches the
+// global 16 bytes that belong at that swizzled position.  Rows past the block
+// end are clamped to its last row: finite data whose scores are masked to -inf
+// and whose softmax weights are 0.  fp32 sources are converted in registers.
+template <int D, bool F32, bool IS_V>
+__device__ __forceinline__ void stage_tile(char* dst, const void* src, int t0, int n, int wave, int lane) {
     using C = Cfg<D>;
 #pragma unroll
-    for (int i = 0; i < C::KUNITS; ++i) {
-        const int u = tid + i * NT;
-        const int row = u / C::DU, c = u % C::DU;
-        const int key = t0 + row;
-        r.k[i] = key < n ? load8<F32>(kp, (int64_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
-    }
-    const int kg = tid / C::DU, dc = tid % C::DU;
-#pragma unroll
-    for (int i = 0; i < C::KPT; ++i) {
-        const int key = t0 + kg * C::KPT + i;
-        r.v[i] = key < n ? load8<F32>(vp, (int64_t)key * D + dc * 8) : u32x4{0, 0, 0, 0};
-    }
-}
-
-// Registers -> LDS stage: K row-major (padded), V transposed + permuted + swizzled.
-template <int D, bool F32>
-__device__ __forceinline__ void store_tile(const TileRegs<D, F32>& r, char* stage, int tid) {
-    using C = Cfg<D>;
-    char* ks = stage;
-    char* vs = stage + C::KSTAGE;
-#pragma unroll
-    for (int i = 0; i < C::KUNITS; ++i) {
-        const int u = tid + i * NT;
-        const int row = u / C::DU, c = u % C::DU;
-        *reinterpret_cast<u32x4*>(ks + row * C::KROW + c * 16) = r.k[i];
-    }
-    const int kg = tid / C::DU, dc = tid % C::DU;
-    const int pos = vt_pos(kg * C::KPT);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int d = dc * 8 + j;
-        char* dst = vs + d * C::VROW + (((pos >> 3) ^ vt_swz(d)) << 4) + ((pos & 7) << 1);
-        const int w = j >> 1;
-        if constexpr (C::KPT == 4) {
-            uint32_t lo, hi;
-            if (j & 1) {
-                lo = (r.v[0][w] >> 16) | (r.v[1][w] & 0xFFFF0000u);
-                hi = (r.v[2][w] >> 16) | (r.v[3][w] & 0xFFFF0000u);
-            } else {
-                lo = (r.v[0][w] & 0xFFFFu) | (r.v[1][w] << 16);
-                hi = (r.v[2][w] & 0xFFFFu) | (r.v[3][w] << 16);
-            }
-            *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+    for (int i = 0; i < C::CPW; ++i) {
+        const int chunk = wave * C::CPW + i;
+        const int p = chunk * 64 + lane;  // 16-byte unit index within the tile
+        const int row = p / C::UPR, phys = p % C::UPR;
+        const int u = IS_V ? v_unit<D>(row, phys) : k_unit<D>(row, phys);
+        const int key = min(t0 + row, n - 1);
+        const int64_t elem = (int64_t)key * D + u * 8;
+        if constexpr (F32) {
+            *reinterpret_cast<u32x4*>(dst + p * 16) = load8<true>(src, elem);
         } else {
-            static_assert(C::KPT == 2, "V keys per thread");
-            uint32_t x;
-            if (j & 1)
-                x = (r.v[0][w] >> 16) | (r.v[1][w] & 0xFFFF0000u);
-            else
-                x = (r.v[0][w] & 0xFFFFu) | (r.v[1][w] << 16);
-            *reinterpret_cast<uint32_t*>(dst) = x;
+            __builtin_amdgcn_global_load_lds(static_cast<const uint16_t*>(src) + elem,
+                                             (LDS_AS void*)(dst + chunk * 1024), 16, 0, 0);
         }
     }
 }
@@ -176,13 +138,13 @@ template <int D, bool F32>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(AttnArgs a) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int h = lane >> 5;   // lane half
-    const int c32 = lane & 31; // query column within the wave's 32
+    const int h = lane >> 5;    // lane half
+    const int c32 = lane & 31;  // query column within the wave's 32
 
     // XCD-aware mapping of workgroup id -> (plane, query tile).
     const int nblk = gridDim.x;
@@ -204,12 +166,16 @@ void attn_fwd_kernel(AttnArgs a) {
     const char* kp = static_cast<const char*>(a.k) + (size_t)(plane * a.kv_plane) * esz;
     const char* vp = static_cast<const char*>(a.v) + (size_t)(plane * a.kv_plane) * esz;
 
-    // Q^T fragments: lane holds q[qrow][16*kk + 8*h .. +7].
+    // Q^T fragments: lane holds q[qrow][16*kk + 8*h .. +7] (rows past Sq read row Sq-1, then zeroed).
     bf16x8 qf[C::NK];
+    {
+        const int64_t qr = qvalid ? qrow : Sq - 1;
 #pragma unroll
-    for (int kk = 0; kk < C::NK; ++kk) {
-        u32x4 x = qvalid ? load8<F32>(qp, qrow * D + kk * 16 + h * 8) : u32x4{0, 0, 0, 0};
-        qf[kk] = __builtin_bit_cast(bf16x8, x);
+        for (int kk = 0; kk < C::NK; ++kk) {
+            u32x4 x = load8<F32>(qp, qr * D + kk * 16 + h * 8);
+            if (!qvalid) x = u32x4{0, 0, 0, 0};
+            qf[kk] = __builtin_bit_cast(bf16x8, x);
+        }
     }
 
     f32x16 o[C::NDB];
@@ -222,34 +188,65 @@ void attn_fwd_kernel(AttnArgs a) {
     float l_run = 0.f;        // this lane's share of the row sum
     const float sl2 = a.scale_log2;
 
+    // Per-lane LDS offsets that do not depend on the tile.
+    // K fragment (S^T A operand): key row kb*32 + c32, d-units 2*kk + h.
+    int k_off[2][C::NK];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < C::NK; ++kk) {
+            const int row = kb * 32 + c32;
+            k_off[kb][kk] = row * C::RB + k_unit<D>(row, 2 * kk + h) * 16;
+        }
+    // V^T fragment (O^T A operand) via ds_read_b64_tr_b16: in each 16-lane
+    // group, lane m = 4a + b reads the 4 values [d0 + 4b, +4) of key row
+    // 16*ks + 8r + 4h + a; the transposed result gives lane i the values at
+    // d0 + i of those 4 keys -- k-slots 8h + 4r .. +3 of the MFMA, which the
+    // S^T accumulator layout assigns to exactly those keys.
+    const int tr_g = lane >> 4, tr_m = lane & 15, tr_a = tr_m >> 2, tr_b = tr_m & 3;
+    int v_off[4][2][C::NDB];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                const int row = 16 * ks + 8 * r + 4 * h + tr_a;
+                const int d0 = 32 * db + 16 * (tr_g & 1) + 4 * tr_b;
+                v_off[ks][r][db] = C::TILE + row * C::RB + v_unit<D>(row, d0 >> 3) * 16 + (d0 & 7) * 2;
+            }
+
     const int ntiles = (n + BN - 1) / BN;
-    TileRegs<D, F32> regs;
     if (ntiles > 0) {
-        load_tile<D, F32>(regs, kp, vp, 0, n, tid);
-        store_tile<D, F32>(regs, smem, tid);
+        stage_tile<D, F32, false>(smem, kp, 0, n, wave, lane);
+        stage_tile<D, F32, true>(smem + C::TILE, vp, 0, n, wave, lane);
     }
-    __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
-        const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile<D, F32>(regs, kp, vp, (t + 1) * BN, n, tid);
-
-        const char* ks = smem + (t & 1) * C::STAGE;
-        const char* vs = ks + C::KSTAGE;
+        // Tile t has landed in LDS for every wave, and every wave is done
+        // reading stage (t+1)&1 from the previous iteration.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 1 < ntiles) {
+            char* nxt = smem + ((t + 1) & 1) * C::STAGE;
+            stage_tile<D, F32, false>(nxt, kp, (t + 1) * BN, n, wave, lane);
+            stage_tile<D, F32, true>(nxt + C::TILE, vp, (t + 1) * BN, n, wave, lane);
+        }
+        const char* st = smem + (t & 1) * C::STAGE;
 
         // S^T (64 keys x 32 queries) = K_tile . Q^T
         f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-            const char* krow = ks + (kb * 32 + c32) * C::KROW + h * 16;
 #pragma unroll
-            for (int kk = 0; kk < C::NK; ++kk) {
-                bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + kk * 32);
+        for (int kk = 0; kk < C::NK; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st + k_off[kb][kk]);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
             }
-        }
 
         // Keys past the end of the block never enter the softmax.
         const int t0 = t * BN;
@@ -263,11 +260,9 @@ void attn_fwd_kernel(AttnArgs a) {
                 }
         }
 
-        float mt = s[0][0];
+        float mt = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[0][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[1][i]);
+        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(s[0][i], s[1][i]));
         mt = pair_max(mt) * sl2;
 
         const bool need = mt > m_run + kSlack;
@@ -296,23 +291,20 @@ void attn_fwd_kernel(AttnArgs a) {
 
         // O^T += V^T . P^T, 16 keys per MFMA.
 #pragma unroll
-        for (int ks16 = 0; ks16 < 4; ++ks16) {
-            const int kb = ks16 >> 1, base = (ks16 & 1) * 8;
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kb = ks >> 1, base = (ks & 1) * 8;
             f32x8 pv = {s[kb][base + 0], s[kb][base + 1], s[kb][base + 2], s[kb][base + 3],
                         s[kb][base + 4], s[kb][base + 5], s[kb][base + 6], s[kb][base + 7]};
             const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-            const int unit = 2 * ks16 + h;
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-                const int d = db * 32 + c32;
-                const bf16x8 vf =
-                    *reinterpret_cast<const bf16x8*>(vs + d * C::VROW + ((unit ^ vt_swz(d)) << 4));
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(st + v_off[ks][0][db]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(st + v_off[ks][1][db]));
+                const s16x4 lohi[2] = {lo, hi};
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, lohi);
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[db], 0, 0, 0);
             }
         }
-
-        if (has_next) store_tile<D, F32>(regs, smem + ((t + 1) & 1) * C::STAGE, tid);
-        __syncthreads();
     }
 
     // Epilogue: normalise, then store or LSE-merge into the accumulator.
