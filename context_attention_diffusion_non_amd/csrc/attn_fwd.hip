@@ -32,6 +32,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace cpattn {
 namespace {
 
@@ -57,12 +59,13 @@ struct Cfg {
     static constexpr int RB = D * 2;            // LDS bytes per K or V row (bf16)
     static constexpr int UPR = D / 8;           // 16-byte units per row
     static constexpr int TILE = BN * RB;        // bytes of one K (or V) tile
-    static constexpr int STAGE = 2 * TILE;      // K tile + V tile
+    static constexpr int LDS = 4 * TILE;        // K stage 0 | K stage 1 | V stage 0 | V stage 1
     static constexpr int CHUNKS = TILE / 1024;  // 1 KB DMA chunks per tile
     static constexpr int CPW = CHUNKS / 4;      // chunks per wave
     static constexpr int NK = D / 16;           // k-steps of the S^T product
     static constexpr int NDB = D / 32;          // 32-row blocks of O^T
     static_assert(CHUNKS % 4 == 0, "tile split over 4 waves");
+    static_assert(LDS <= 65536, "stage offsets must fit the 16-bit LDS immediate");
 };
 
 // XOR swizzles of the 16-byte units of a row (rows are unpadded).
@@ -108,41 +111,83 @@ __device__ __forceinline__ u32x4 load8(const void* base, int64_t elem) {
     }
 }
 
-// Stage one K or V tile (keys t0 .. t0+63) into LDS.  bf16 sources go
-// global -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes
-// bytes [16 l, 16 l + 16) of the wave's 1 KB chunk); each lane fetches the
-// global 16 bytes that belong at that swizzled position.  Rows past the block
-// end are clamped to its last row: finite data whose scores are masked to -inf
-// and whose softmax weights are 0.  fp32 sources are converted in registers.
-template <int D, bool F32, bool IS_V>
-__device__ __forceinline__ void stage_tile(char* dst, const void* src, int t0, int n, int wave, int lane) {
-    using C = Cfg<D>;
+// Per-lane constants of the tile DMA: LDS DMA (global_load_lds_dwordx4)
+// writes lane l's 16 bytes at byte 16 l of the wave's 1 KB chunk, so each lane
+// fetches the global 16 bytes that belong at that swizzled LDS position: unit
+// p = 64 * chunk + l of the tile is row p / UPR, physical unit p % UPR.
+template <int D, bool IS_V>
+struct DmaLane {
+    uint32_t off[Cfg<D>::CPW];  // byte offset of the lane's 16 bytes within the tile's global rows
+    int row[Cfg<D>::CPW];       // tile row of those bytes
+    __device__ __forceinline__ void init(int wave, int lane) {
+        using C = Cfg<D>;
 #pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
-        const int chunk = wave * C::CPW + i;
-        const int p = chunk * 64 + lane;  // 16-byte unit index within the tile
-        const int row = p / C::UPR, phys = p % C::UPR;
-        const int u = IS_V ? v_unit<D>(row, phys) : k_unit<D>(row, phys);
-        const int key = min(t0 + row, n - 1);
-        const int64_t elem = (int64_t)key * D + u * 8;
-        if constexpr (F32) {
-            *reinterpret_cast<u32x4*>(dst + p * 16) = load8<true>(src, elem);
-        } else {
-            __builtin_amdgcn_global_load_lds(static_cast<const uint16_t*>(src) + elem,
-                                             (LDS_AS void*)(dst + chunk * 1024), 16, 0, 0);
+        for (int i = 0; i < C::CPW; ++i) {
+            const int p = (wave * C::CPW + i) * 64 + lane;
+            const int r = p / C::UPR, phys = p % C::UPR;
+            const int u = IS_V ? v_unit<D>(r, phys) : k_unit<D>(r, phys);
+            row[i] = r;
+            off[i] = (uint32_t)(r * C::RB + u * 16);
         }
     }
+};
+
+// Stage one K or V tile (keys t0 .. t0+63 of a block of n keys) into the LDS
+// region at byte `lds_off`.  bf16 sources go global -> LDS directly; rows past
+// the block end are clamped to its last row (finite data whose scores are
+// masked to -inf and whose softmax weights are 0).  fp32 sources are read into
+// registers, rounded to bf16 and stored.  `wave` must be wave-uniform (it
+// selects the LDS chunk, which the DMA takes from M0).
+template <int D, bool F32, bool IS_V>
+__device__ __forceinline__ void stage_tile(char* smem, int lds_off, const char* src, int t0, int n,
+                                           const DmaLane<D, IS_V>& dl, int wave, int lane) {
+    using C = Cfg<D>;
+    const char* tile = src + (size_t)t0 * (F32 ? 2 * C::RB : C::RB);
+    char* dst0 = smem + lds_off + wave * C::CPW * 1024;
+    if (t0 + BN <= n) {
+#pragma unroll
+        for (int i = 0; i < C::CPW; ++i) {
+            if constexpr (F32) {
+                *reinterpret_cast<u32x4*>(dst0 + i * 1024 + lane * 16) = load8<true>(tile, dl.off[i] / 2);
+            } else {
+                __builtin_amdgcn_global_load_lds(tile + dl.off[i], (LDS_AS void*)(dst0 + i * 1024), 16, 0, 0);
+            }
+        }
+    } else {
+        const int last = n - 1 - t0;
+#pragma unroll
+        for (int i = 0; i < C::CPW; ++i) {
+            const uint32_t off = dl.off[i] - (uint32_t)((dl.row[i] - min(dl.row[i], last)) * C::RB);
+            if constexpr (F32) {
+                *reinterpret_cast<u32x4*>(dst0 + i * 1024 + lane * 16) = load8<true>(tile, off / 2);
+            } else {
+                __builtin_amdgcn_global_load_lds(tile + off, (LDS_AS void*)(dst0 + i * 1024), 16, 0, 0);
+            }
+        }
+    }
+}
+
+// Row max of a 64-key tile (both lane halves), in log2 units.
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float sl2) {
+    float m[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = fmaxf(s[0][j], s[1][j]);
+#pragma unroll
+    for (int i = 4; i < 16; i += 4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = fmaxf(m[j], fmaxf(s[0][i + j], s[1][i + j]));
+    return pair_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]))) * sl2;
 }
 
 template <int D, bool F32>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(AttnArgs a) {
     using C = Cfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int h = lane >> 5;    // lane half
     const int c32 = lane & 31;  // query column within the wave's 32
 
@@ -188,51 +233,54 @@ void attn_fwd_kernel(AttnArgs a) {
     float l_run = 0.f;        // this lane's share of the row sum
     const float sl2 = a.scale_log2;
 
-    // Per-lane LDS offsets that do not depend on the tile.
-    // K fragment (S^T A operand): key row kb*32 + c32, d-units 2*kk + h.
-    int k_off[2][C::NK];
+    // Per-lane LDS read offsets (tile-relative); stage and (kb, ks, r) parts are immediates.
+    // K fragment (S^T A operand): key row kb*32 + c32, d-units 2*kk + h; the
+    // swizzle depends on the row only through c32.
+    int k_lane[C::NK];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int kk = 0; kk < C::NK; ++kk) {
-            const int row = kb * 32 + c32;
-            k_off[kb][kk] = row * C::RB + k_unit<D>(row, 2 * kk + h) * 16;
-        }
+    for (int kk = 0; kk < C::NK; ++kk) k_lane[kk] = c32 * C::RB + k_unit<D>(c32, 2 * kk + h) * 16;
     // V^T fragment (O^T A operand) via ds_read_b64_tr_b16: in each 16-lane
     // group, lane m = 4a + b reads the 4 values [d0 + 4b, +4) of key row
     // 16*ks + 8r + 4h + a; the transposed result gives lane i the values at
     // d0 + i of those 4 keys -- k-slots 8h + 4r .. +3 of the MFMA, which the
-    // S^T accumulator layout assigns to exactly those keys.
-    const int tr_g = lane >> 4, tr_m = lane & 15, tr_a = tr_m >> 2, tr_b = tr_m & 3;
-    int v_off[4][2][C::NDB];
+    // S^T accumulator layout assigns to exactly those keys.  The swizzle
+    // depends on the row only through 4h + a.
+    int v_lane[C::NDB];
+    {
+        const int tr_g = lane >> 4, tr_m = lane & 15, tr_a = tr_m >> 2, tr_b = tr_m & 3;
+        const int row = 4 * h + tr_a;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int db = 0; db < C::NDB; ++db) {
-                const int row = 16 * ks + 8 * r + 4 * h + tr_a;
-                const int d0 = 32 * db + 16 * (tr_g & 1) + 4 * tr_b;
-                v_off[ks][r][db] = C::TILE + row * C::RB + v_unit<D>(row, d0 >> 3) * 16 + (d0 & 7) * 2;
-            }
+        for (int db = 0; db < C::NDB; ++db) {
+            const int d0 = 32 * db + 16 * (tr_g & 1) + 4 * tr_b;
+            v_lane[db] = row * C::RB + v_unit<D>(row, d0 >> 3) * 16 + (d0 & 7) * 2;
+        }
+    }
+    DmaLane<D, false> kdl;
+    DmaLane<D, true> vdl;
+    kdl.init(wave, lane);
+    vdl.init(wave, lane);
 
     const int ntiles = (n + BN - 1) / BN;
     if (ntiles > 0) {
-        stage_tile<D, F32, false>(smem, kp, 0, n, wave, lane);
-        stage_tile<D, F32, true>(smem + C::TILE, vp, 0, n, wave, lane);
+        stage_tile<D, F32, false>(smem, 0, kp, 0, n, kdl, wave, lane);
+        stage_tile<D, F32, true>(smem, 2 * C::TILE, vp, 0, n, vdl, wave, lane);
     }
 
-    for (int t = 0; t < ntiles; ++t) {
-        // Tile t has landed in LDS for every wave, and every wave is done
-        // reading stage (t+1)&1 from the previous iteration.
+    // One tile: wait for its DMA, start the next tile's DMA into the other
+    // stage, S^T = K Q^T, softmax, O^T += V^T P^T.  STG (the stage holding the
+    // tile) is a compile-time constant, so every LDS address is a per-lane
+    // base plus an immediate.
+    auto step = [&](auto stg_c, int t) __attribute__((always_inline)) {
+        constexpr int STG = decltype(stg_c)::value;
+        constexpr int K_CUR = STG * C::TILE, V_CUR = (2 + STG) * C::TILE;
+        constexpr int K_NXT = (1 - STG) * C::TILE, V_NXT = (3 - STG) * C::TILE;
+        // tile t has landed for every wave; every wave is done with the other stage
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t + 1 < ntiles) {
-            char* nxt = smem + ((t + 1) & 1) * C::STAGE;
-            stage_tile<D, F32, false>(nxt, kp, (t + 1) * BN, n, wave, lane);
-            stage_tile<D, F32, true>(nxt + C::TILE, vp, (t + 1) * BN, n, wave, lane);
+            stage_tile<D, F32, false>(smem, K_NXT, kp, (t + 1) * BN, n, kdl, wave, lane);
+            stage_tile<D, F32, true>(smem, V_NXT, vp, (t + 1) * BN, n, vdl, wave, lane);
         }
-        const char* st = smem + (t & 1) * C::STAGE;
 
         // S^T (64 keys x 32 queries) = K_tile . Q^T
         f32x16 s[2];
@@ -244,7 +292,7 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int kk = 0; kk < C::NK; ++kk)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st + k_off[kb][kk]);
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + K_CUR + kb * 32 * C::RB + k_lane[kk]);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
             }
 
@@ -260,11 +308,7 @@ void attn_fwd_kernel(AttnArgs a) {
                 }
         }
 
-        float mt = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(s[0][i], s[1][i]));
-        mt = pair_max(mt) * sl2;
-
+        const float mt = tile_max(s, sl2);
         const bool need = mt > m_run + kSlack;
         float alpha = 1.f;
         if (need) {
@@ -272,16 +316,22 @@ void attn_fwd_kernel(AttnArgs a) {
             m_run = mt;
         }
         const float neg_m = -m_run;
-        float rs = 0.f;
+        float rs0 = 0.f, rs1 = 0.f;
+        bf16x8 pb[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kb = ks >> 1, base = (ks & 1) * 8;
+            f32x8 p;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = exp2_fast(fmaf(s[kb][i], sl2, neg_m));
-                s[kb][i] = p;
-                rs += p;
+            for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(s[kb][base + j], sl2, neg_m));
+            pb[ks] = __builtin_convertvector(p, bf16x8);
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                rs0 += p[j];
+                rs1 += p[j + 1];
             }
-        l_run = l_run * alpha + rs;
+        }
+        l_run = l_run * alpha + (rs0 + rs1);
         if (__any(need)) {
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db)
@@ -292,19 +342,21 @@ void attn_fwd_kernel(AttnArgs a) {
         // O^T += V^T . P^T, 16 keys per MFMA.
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int kb = ks >> 1, base = (ks & 1) * 8;
-            f32x8 pv = {s[kb][base + 0], s[kb][base + 1], s[kb][base + 2], s[kb][base + 3],
-                        s[kb][base + 4], s[kb][base + 5], s[kb][base + 6], s[kb][base + 7]};
-            const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(st + v_off[ks][0][db]));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(st + v_off[ks][1][db]));
+                const char* vb = smem + V_CUR + 16 * ks * C::RB + v_lane[db];
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vb));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vb + 8 * C::RB));
                 const s16x4 lohi[2] = {lo, hi};
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, lohi);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], o[db], 0, 0, 0);
             }
         }
+    };
+
+    for (int t = 0; t < ntiles; t += 2) {
+        step(std::integral_constant<int, 0>(), t);
+        if (t + 1 < ntiles) step(std::integral_constant<int, 1>(), t + 1);
     }
 
     // Epilogue: normalise, then store or LSE-merge into the accumulator.
