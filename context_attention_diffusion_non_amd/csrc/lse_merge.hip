@@ -6,7 +6,8 @@
 // A side whose LSE is -inf contributes exactly nothing (its output values are
 // not read into the result), and two empty sides give 0 and -inf.
 //
-// HBM-bound: every byte is touched once.  Each thread merges float4 pieces;
+// HBM-bound: every byte is touched once, so the row data moves with
+// non-temporal loads and stores.  Each thread merges float4 pieces;
 // a wave covers whole rows (d is a power of two <= 256), so the in-place LSE
 // update by the row's first lane cannot race with another wave reading it.
 #include "internal.h"
@@ -35,11 +36,13 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a, int64_t n_it
         item[u] = ((int64_t)blockIdx.x * UNR + u) * NT + threadIdx.x;
         if (item[u] < n_items) {
             const int64_t row = item[u] >> shift;
-            acc[u] = *reinterpret_cast<const f32x4*>(a.acc_out + item[u] * 4);
+            acc[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.acc_out + item[u] * 4));
             if constexpr (BLK_F32) {
-                blk[u] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.blk_out) + item[u] * 4);
+                blk[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4*>(static_cast<const float*>(a.blk_out) + item[u] * 4));
             } else {
-                const bf16x4 b = *reinterpret_cast<const bf16x4*>(static_cast<const __bf16*>(a.blk_out) + item[u] * 4);
+                const bf16x4 b = __builtin_nontemporal_load(
+                    reinterpret_cast<const bf16x4*>(static_cast<const __bf16*>(a.blk_out) + item[u] * 4));
                 blk[u] = __builtin_convertvector(b, f32x4);
             }
             la[u] = a.acc_lse[row];
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a, int64_t n_it
         f32x4 r = {0.f, 0.f, 0.f, 0.f};
         if (wa != 0.f) r = acc[u] * wa;
         if (wb != 0.f) r = r + blk[u] * wb;
-        *reinterpret_cast<f32x4*>(a.acc_out + item[u] * 4) = r;
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(a.acc_out + item[u] * 4));
         if ((item[u] & ((1 << shift) - 1)) == 0) a.acc_lse[item[u] >> shift] = lnew;
     }
 }
