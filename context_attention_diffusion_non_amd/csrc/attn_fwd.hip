@@ -295,6 +295,15 @@ void attn_fwd_kernel(AttnArgs a) {
                 const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + K_CUR + kb * 32 * C::RB + k_lane[kk]);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
             }
+        // keep four K-fragment reads in flight ahead of the MFMAs that consume them
+#pragma unroll
+        for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
         // Keys past the end of the block never enter the softmax.
         const int t0 = t * BN;
