@@ -15,6 +15,7 @@ HEADER = os.path.join(_ROOT, "include", "cpattn.h")
 
 BF16 = 0
 FP32 = 1
+FP16 = 2
 
 STATUS = {
     0: "CPATTN_OK", 1: "CPATTN_ERR_NULL", 2: "CPATTN_ERR_SHAPE", 3: "CPATTN_ERR_DEGREE",

@@ -29,7 +29,11 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(CPATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
-bool valid_dtype(int dt) { return dt == CPATTN_BF16 || dt == CPATTN_FP32; }
+static_assert((int)CPATTN_BF16 == (int)cpattn::DT_BF16 && (int)CPATTN_FP32 == (int)cpattn::DT_F32 &&
+                  (int)CPATTN_FP16 == (int)cpattn::DT_F16,
+              "cpattn_dtype and the kernels' element types must agree");
+
+bool valid_dtype(int dt) { return dt == CPATTN_BF16 || dt == CPATTN_FP32 || dt == CPATTN_FP16; }
 size_t dtype_bytes(int dt) { return dt == CPATTN_FP32 ? 4 : 2; }
 
 // Byte ranges [p, p+n) and [q, q+m) intersect (empty ranges never do).
@@ -115,8 +119,8 @@ cpattn::AttnArgs make_args(const void* q, const void* k, const void* v, void* ou
     a.kv_plane = kv_ld * d;
     a.scale_log2 = resolve_scale(scale, d) * 1.4426950408889634f;
     a.mode = cpattn::EPI_STORE;
-    a.out_fp32 = out_dt == CPATTN_FP32;
-    a.in_fp32 = in_dt == CPATTN_FP32;
+    a.out_dtype = out_dt;
+    a.in_dtype = in_dt;
     a.d = (int)d;
     return a;
 }
@@ -173,7 +177,7 @@ CPATTN_EXPORT int cpattn_lse_merge(float* acc_out, float* acc_lse, const void* b
         overlaps(acc_out, acc_b, acc_lse, lse_b))
         return fail(CPATTN_ERR_ALIAS, "merge operands overlap");
     if ((rows * d / 4 + 1023) / 1024 > kMaxBlocks) return fail(CPATTN_ERR_SHAPE, "merge too large");
-    cpattn::MergeArgs a{acc_out, acc_lse, blk_out, blk_lse, rows, d, blk_dtype == CPATTN_FP32};
+    cpattn::MergeArgs a{acc_out, acc_lse, blk_out, blk_lse, rows, d, blk_dtype};
     const hipError_t e = cpattn::launch_lse_merge(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return CPATTN_OK;
@@ -248,10 +252,10 @@ CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, v
         }
         if (last) {
             a.out = out;
-            a.out_fp32 = out_dtype == CPATTN_FP32;
+            a.out_dtype = out_dtype;
         } else {
             a.out = acc;
-            a.out_fp32 = 1;
+            a.out_dtype = cpattn::DT_F32;
         }
         const hipError_t e = cpattn::launch_attn_fwd(a, s);
         if (e != hipSuccess) return hip_fail(e, "attention kernel launch (ring chunk)");

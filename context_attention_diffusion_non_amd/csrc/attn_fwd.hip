@@ -11,7 +11,8 @@
 //
 // Design (one workgroup = 4 waves = 128 query rows of one plane):
 //   * Everything is computed transposed: S^T = K Q^T and O^T = V^T P^T with
-//     v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane then
+//     v_mfma_f32_32x32x16_bf16 (or its f16 twin for fp16 inputs, where P is
+//     rounded to fp16 instead of bf16).  In the 32x32 accumulator layout a lane then
 //     owns one query column and 16 of every 32 keys, so the row max / row sum
 //     need one cross-half exchange (v_permlane32_swap) and the per-query
 //     rescale of O is lane-local.
@@ -39,6 +40,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -94,13 +97,32 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// 16-bit operand element of the MFMA path for an input element type: fp16
+// inputs run on the f16 MFMA, bf16 and fp32 inputs on the bf16 one.
+template <int IN>
+struct Op {
+    typedef __bf16 T8 __attribute__((ext_vector_type(8)));
+};
+template <>
+struct Op<DT_F16> {
+    typedef _Float16 T8 __attribute__((ext_vector_type(8)));
+};
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 cvt8_f32_bf16(f32x4 a, f32x4 b) {
     f32x8 f = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     bf16x8 h = __builtin_convertvector(f, bf16x8);
     return __builtin_bit_cast(u32x4, h);
 }
 
-// 8 consecutive elements of a row as bf16 bits, from a bf16 or fp32 buffer.
+// 8 consecutive elements of a row as 16-bit operand bits: fp32 buffers are
+// rounded to bf16, bf16 and fp16 buffers are taken as they are.
 template <bool F32>
 __device__ __forceinline__ u32x4 load8(const void* base, int64_t elem) {
     if constexpr (F32) {
@@ -109,6 +131,14 @@ __device__ __forceinline__ u32x4 load8(const void* base, int64_t elem) {
     } else {
         return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem);
     }
+}
+
+// 16 bytes per lane global -> LDS (global_load_lds_dwordx4): lane l's bytes
+// land at byte 16 l of the 1 KB at `lds`.  Kept out of the templates below:
+// the host pass of hipcc rejects the builtin in a template body instantiated
+// from more than one kernel.
+__device__ __forceinline__ void dma16(const char* g, char* lds) {
+    __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds, 16, 0, 0);
 }
 
 // Per-lane constants of the tile DMA: LDS DMA (global_load_lds_dwordx4)
@@ -135,10 +165,11 @@ struct DmaLane {
 // Stage one K or V tile (keys t0 .. t0+63 of a block of n keys) into the LDS
 // region at byte `lds_off`.  bf16 sources go global -> LDS directly; rows past
 // the block end are clamped to its last row (finite data whose scores are
-// masked to -inf and whose softmax weights are 0).  fp32 sources are read into
-// registers, rounded to bf16 and stored.  `wave` must be wave-uniform (it
+// masked to -inf and whose softmax weights are 0).  fp16 sources take the bf16
+// path (16-bit elements either way).  fp32 sources are read into registers,
+// rounded to bf16 and stored.  `wave` must be wave-uniform (it
 // selects the LDS chunk, which the DMA takes from M0).
-template <int D, bool F32, bool IS_V>
+template <bool F32, int D, bool IS_V>
 __device__ __forceinline__ void stage_tile(char* smem, int lds_off, const char* src, int t0, int n,
                                            const DmaLane<D, IS_V>& dl, int wave, int lane) {
     using C = Cfg<D>;
@@ -150,7 +181,7 @@ __device__ __forceinline__ void stage_tile(char* smem, int lds_off, const char* 
             if constexpr (F32) {
                 *reinterpret_cast<u32x4*>(dst0 + i * 1024 + lane * 16) = load8<true>(tile, dl.off[i] / 2);
             } else {
-                __builtin_amdgcn_global_load_lds(tile + dl.off[i], (LDS_AS void*)(dst0 + i * 1024), 16, 0, 0);
+                dma16(tile + dl.off[i], dst0 + i * 1024);
             }
         }
     } else {
@@ -161,7 +192,7 @@ __device__ __forceinline__ void stage_tile(char* smem, int lds_off, const char* 
             if constexpr (F32) {
                 *reinterpret_cast<u32x4*>(dst0 + i * 1024 + lane * 16) = load8<true>(tile, off / 2);
             } else {
-                __builtin_amdgcn_global_load_lds(tile + off, (LDS_AS void*)(dst0 + i * 1024), 16, 0, 0);
+                dma16(tile + off, dst0 + i * 1024);
             }
         }
     }
@@ -179,10 +210,12 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float sl2) {
     return pair_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]))) * sl2;
 }
 
-template <int D, bool F32>
+template <int D, int IN>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(AttnArgs a) {
     using C = Cfg<D>;
+    constexpr bool F32 = IN == DT_F32;
+    typedef typename Op<IN>::T8 op8;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
     const int tid = threadIdx.x;
@@ -212,14 +245,14 @@ void attn_fwd_kernel(AttnArgs a) {
     const char* vp = static_cast<const char*>(a.v) + (size_t)(plane * a.kv_plane) * esz;
 
     // Q^T fragments: lane holds q[qrow][16*kk + 8*h .. +7] (rows past Sq read row Sq-1, then zeroed).
-    bf16x8 qf[C::NK];
+    op8 qf[C::NK];
     {
         const int64_t qr = qvalid ? qrow : Sq - 1;
 #pragma unroll
         for (int kk = 0; kk < C::NK; ++kk) {
             u32x4 x = load8<F32>(qp, qr * D + kk * 16 + h * 8);
             if (!qvalid) x = u32x4{0, 0, 0, 0};
-            qf[kk] = __builtin_bit_cast(bf16x8, x);
+            qf[kk] = __builtin_bit_cast(op8, x);
         }
     }
 
@@ -262,8 +295,8 @@ void attn_fwd_kernel(AttnArgs a) {
 
     const int ntiles = (n + BN - 1) / BN;
     if (ntiles > 0) {
-        stage_tile<D, F32, false>(smem, 0, kp, 0, n, kdl, wave, lane);
-        stage_tile<D, F32, true>(smem, 2 * C::TILE, vp, 0, n, vdl, wave, lane);
+        stage_tile<F32>(smem, 0, kp, 0, n, kdl, wave, lane);
+        stage_tile<F32>(smem, 2 * C::TILE, vp, 0, n, vdl, wave, lane);
     }
 
     // One tile: wait for its DMA, start the next tile's DMA into the other
@@ -278,8 +311,8 @@ void attn_fwd_kernel(AttnArgs a) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t + 1 < ntiles) {
-            stage_tile<D, F32, false>(smem, K_NXT, kp, (t + 1) * BN, n, kdl, wave, lane);
-            stage_tile<D, F32, true>(smem, V_NXT, vp, (t + 1) * BN, n, vdl, wave, lane);
+            stage_tile<F32>(smem, K_NXT, kp, (t + 1) * BN, n, kdl, wave, lane);
+            stage_tile<F32>(smem, V_NXT, vp, (t + 1) * BN, n, vdl, wave, lane);
         }
 
         // S^T (64 keys x 32 queries) = K_tile . Q^T
@@ -292,8 +325,8 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int kk = 0; kk < C::NK; ++kk)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + K_CUR + kb * 32 * C::RB + k_lane[kk]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+                const op8 kf = *reinterpret_cast<const op8*>(smem + K_CUR + kb * 32 * C::RB + k_lane[kk]);
+                s[kb] = mfma32x32x16(kf, qf[kk], s[kb]);
             }
         // keep four K-fragment reads in flight ahead of the MFMAs that consume them
 #pragma unroll
@@ -326,14 +359,14 @@ void attn_fwd_kernel(AttnArgs a) {
         }
         const float neg_m = -m_run;
         float rs0 = 0.f, rs1 = 0.f;
-        bf16x8 pb[4];
+        op8 pb[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kb = ks >> 1, base = (ks & 1) * 8;
             f32x8 p;
 #pragma unroll
             for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(s[kb][base + j], sl2, neg_m));
-            pb[ks] = __builtin_convertvector(p, bf16x8);
+            pb[ks] = __builtin_convertvector(p, op8);
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
                 rs0 += p[j];
@@ -357,8 +390,8 @@ void attn_fwd_kernel(AttnArgs a) {
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vb));
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(vb + 8 * C::RB));
                 const s16x4 lohi[2] = {lo, hi};
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, lohi);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], o[db], 0, 0, 0);
+                const op8 vf = __builtin_bit_cast(op8, lohi);
+                o[db] = mfma32x32x16(vf, pb[ks], o[db]);
             }
         }
     };
@@ -397,41 +430,63 @@ void attn_fwd_kernel(AttnArgs a) {
     }
 
     const size_t orow = (size_t)(plane * Sq + qrow) * D;
+    // lane owns d-values db*32 + g4*8 + h*4 .. +3 of its query row
+    f32x4 r[C::NDB * 4];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = db * 32 + g4 * 8 + h * 4;
-            f32x4 r = {o[db][g4 * 4 + 0] * wb, o[db][g4 * 4 + 1] * wb, o[db][g4 * 4 + 2] * wb,
+            f32x4 x = {o[db][g4 * 4 + 0] * wb, o[db][g4 * 4 + 1] * wb, o[db][g4 * 4 + 2] * wb,
                        o[db][g4 * 4 + 3] * wb};
             if (acc != nullptr && wa != 0.f) {
-                const f32x4 av = *reinterpret_cast<const f32x4*>(acc + d0);
-                r = r + av * wa;
+                const f32x4 av = *reinterpret_cast<const f32x4*>(acc + db * 32 + g4 * 8 + h * 4);
+                x = x + av * wa;
             }
-            if (a.out_fp32) {
-                *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + d0) = r;
-            } else {
-                const bf16x4 b = __builtin_convertvector(r, bf16x4);
-                *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + orow + d0) = b;
-            }
+            r[db * 4 + g4] = x;
         }
+    if (a.out_dtype == DT_F32) {
+        float* dst = static_cast<float*>(a.out) + orow + h * 4;
+#pragma unroll
+        for (int i = 0; i < C::NDB * 4; ++i) *reinterpret_cast<f32x4*>(dst + i * 8) = r[i];
+    } else if (a.out_dtype == DT_F16) {
+        _Float16* dst = static_cast<_Float16*>(a.out) + orow + h * 4;
+#pragma unroll
+        for (int i = 0; i < C::NDB * 4; ++i)
+            *reinterpret_cast<f16x4*>(dst + i * 8) = __builtin_convertvector(r[i], f16x4);
+    } else {
+        __bf16* dst = static_cast<__bf16*>(a.out) + orow + h * 4;
+#pragma unroll
+        for (int i = 0; i < C::NDB * 4; ++i)
+            *reinterpret_cast<bf16x4*>(dst + i * 8) = __builtin_convertvector(r[i], bf16x4);
+    }
     if (h == 0) a.lse_out[plane * Sq + qrow] = lnew2 * kLn2;
 }
 
-template <int D, bool F32>
+template <int D, int IN>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
     const int64_t nq = (a.Sq + BM - 1) / BM;
     const int64_t nblk = nq * a.n_planes;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, F32>), dim3((unsigned)nblk), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, IN>), dim3((unsigned)nblk), dim3(NT), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t stream) {
+    switch (a.in_dtype) {
+        case DT_BF16: return launch_t<D, DT_BF16>(a, stream);
+        case DT_F32: return launch_t<D, DT_F32>(a, stream);
+        case DT_F16: return launch_t<D, DT_F16>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream) {
     if (a.Sq <= 0 || a.n_planes <= 0) return hipSuccess;
-    if (a.d == 128) return a.in_fp32 ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
-    if (a.d == 64) return a.in_fp32 ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
+    if (a.out_dtype != DT_BF16 && a.out_dtype != DT_F32 && a.out_dtype != DT_F16) return hipErrorInvalidValue;
+    if (a.d == 128) return launch_d<128>(a, stream);
+    if (a.d == 64) return launch_d<64>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -6,6 +6,13 @@
 
 namespace cpattn {
 
+// Element types of tensors crossing the kernels (same values as cpattn_dtype).
+enum ElemType : int {
+    DT_BF16 = 0,
+    DT_F32 = 1,
+    DT_F16 = 2,
+};
+
 // Epilogue of the attention kernel.
 enum AttnEpilogue : int {
     EPI_STORE = 0,  // write the chunk's own (out, lse)
@@ -16,7 +23,7 @@ struct AttnArgs {
     const void* q;
     const void* k;
     const void* v;
-    void* out;             // destination: out_fp32 ? float : bf16, [planes, Sq, D]
+    void* out;             // destination of element type out_dtype, [planes, Sq, D]
     float* lse_out;        // [planes, Sq]
     const float* acc_in;   // EPI_MERGE: fp32 accumulator [planes, Sq, D] (may equal out)
     const float* lse_in;   // EPI_MERGE: accumulator LSE [planes, Sq] (may equal lse_out)
@@ -26,8 +33,8 @@ struct AttnArgs {
     int64_t kv_plane;      // elements between consecutive K/V planes (kv_ld * D)
     float scale_log2;      // softmax scale * log2(e)
     int mode;              // AttnEpilogue
-    int out_fp32;          // 1: fp32 destination, 0: bf16
-    int in_fp32;           // 1: q/k/v are fp32 (rounded to bf16 on staging)
+    int out_dtype;         // ElemType of out
+    int in_dtype;          // ElemType of q/k/v (DT_F32 is rounded to bf16 on staging)
     int d;                 // 64 or 128
 };
 
@@ -40,7 +47,7 @@ struct MergeArgs {
     const float* blk_lse;
     int64_t rows;
     int64_t d;
-    int blk_fp32;          // 1: blk_out fp32, 0: bf16
+    int blk_dtype;         // ElemType of blk_out
 };
 
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);

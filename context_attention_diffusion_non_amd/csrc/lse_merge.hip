@@ -19,13 +19,14 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;
 constexpr int UNR = 4;  // float4 pieces per thread
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <bool BLK_F32>
+template <int BLK>
 __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a, int64_t n_items, int shift) {
     // shift = log2(d / 4): items per row is a power of two
     f32x4 acc[UNR], blk[UNR];
@@ -37,9 +38,13 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a, int64_t n_it
         if (item[u] < n_items) {
             const int64_t row = item[u] >> shift;
             acc[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.acc_out + item[u] * 4));
-            if constexpr (BLK_F32) {
+            if constexpr (BLK == DT_F32) {
                 blk[u] = __builtin_nontemporal_load(
                     reinterpret_cast<const f32x4*>(static_cast<const float*>(a.blk_out) + item[u] * 4));
+            } else if constexpr (BLK == DT_F16) {
+                const f16x4 b = __builtin_nontemporal_load(
+                    reinterpret_cast<const f16x4*>(static_cast<const _Float16*>(a.blk_out) + item[u] * 4));
+                blk[u] = __builtin_convertvector(b, f32x4);
             } else {
                 const bf16x4 b = __builtin_nontemporal_load(
                     reinterpret_cast<const bf16x4*>(static_cast<const __bf16*>(a.blk_out) + item[u] * 4));
@@ -80,10 +85,19 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
     while ((int64_t(1) << shift) < per_row) ++shift;
     const int64_t n_items = a.rows * per_row;
     const int64_t nblk = (n_items + (int64_t)NT * UNR - 1) / ((int64_t)NT * UNR);
-    if (a.blk_fp32)
-        hipLaunchKernelGGL((lse_merge_kernel<true>), dim3((unsigned)nblk), dim3(NT), 0, stream, a, n_items, shift);
-    else
-        hipLaunchKernelGGL((lse_merge_kernel<false>), dim3((unsigned)nblk), dim3(NT), 0, stream, a, n_items, shift);
+    switch (a.blk_dtype) {
+        case DT_F32:
+            hipLaunchKernelGGL((lse_merge_kernel<DT_F32>), dim3((unsigned)nblk), dim3(NT), 0, stream, a, n_items, shift);
+            break;
+        case DT_F16:
+            hipLaunchKernelGGL((lse_merge_kernel<DT_F16>), dim3((unsigned)nblk), dim3(NT), 0, stream, a, n_items, shift);
+            break;
+        case DT_BF16:
+            hipLaunchKernelGGL((lse_merge_kernel<DT_BF16>), dim3((unsigned)nblk), dim3(NT), 0, stream, a, n_items, shift);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -12,14 +12,14 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import BF16, FP32, CpattnError, check
+from ._lib import BF16, FP16, FP32, CpattnError, check
 
-_DT = {torch.bfloat16: BF16, torch.float32: FP32}
+_DT = {torch.bfloat16: BF16, torch.float32: FP32, torch.float16: FP16}
 
 
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype not in _DT:
-        raise TypeError(f"unsupported dtype {t.dtype}; cpattn takes bfloat16 or float32")
+        raise TypeError(f"unsupported dtype {t.dtype}; cpattn takes bfloat16, float16 or float32")
     return _DT[t.dtype]
 
 
@@ -147,4 +147,4 @@ def ulysses_permute(x: torch.Tensor, degree: int, group: int = 0, direction: int
 
 
 __all__ = ["block_fwd", "lse_merge", "ring_fwd", "ring_fwd_workspace_bytes", "ulysses_permute", "CpattnError",
-           "BF16", "FP32"]
+           "BF16", "FP16", "FP32"]

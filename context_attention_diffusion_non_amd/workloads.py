@@ -159,11 +159,19 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
 
 
 def random_bhsd(seed: int, shape, dtype: str = "bf16", scale: float = 1.0):
-    """Small helper for tests: N(0, scale^2) of ``shape``; returns (values_f32, bits_or_None)."""
+    """Small helper for tests: N(0, scale^2) of ``shape``.
+
+    Returns (values_f32, storage): storage is None for "fp32", the bf16 bit
+    patterns (uint16, nearest-even) for "bf16", and the float16 array
+    (numpy's nearest-even cast) for "fp16"; values_f32 holds the rounded values.
+    """
     rng = np.random.Generator(np.random.PCG64(seed))
     x = (rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)).astype(np.float32)
     if dtype == "fp32":
         return x, None
+    if dtype == "fp16":
+        h = x.astype(np.float16)
+        return h.astype(np.float32), h
     b = bf16_round_bits(x)
     return bf16_bits_to_f32(b), b
 

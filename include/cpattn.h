@@ -38,8 +38,9 @@ extern "C" {
 #endif
 
 typedef enum {
-    CPATTN_BF16 = 0, /* bfloat16: attention inputs/outputs */
-    CPATTN_FP32 = 1  /* float32: inputs are rounded to bf16 (nearest-even) when staged for the MFMA path */
+    CPATTN_BF16 = 0, /* bfloat16: attention inputs/outputs; products on the bf16 MFMA, P rounded to bf16 */
+    CPATTN_FP32 = 1, /* float32: inputs are rounded to bf16 (nearest-even) when staged for the MFMA path */
+    CPATTN_FP16 = 2  /* float16: inputs/outputs; products on the fp16 MFMA, P rounded to fp16 */
 } cpattn_dtype;
 
 typedef enum {
@@ -69,8 +70,10 @@ typedef enum {
  *        of the buffer, rows [0, Skv) are used, rows are d contiguous elements.
  *        kv_ld >= Skv lets a chunk of a larger resident K/V buffer be passed in
  *        place (pointer advanced to the chunk's first row).
+ *   q, k, v share in_dtype (CPATTN_BF16, CPATTN_FP16 or CPATTN_FP32).
  *   out  [B, H, Sq, d]  out_dtype (CPATTN_FP32 keeps the partial in fp32, the
- *        convert_to_fp32 ring numerics; CPATTN_BF16 rounds to nearest-even).
+ *        convert_to_fp32 ring numerics; CPATTN_BF16 / CPATTN_FP16 round to
+ *        nearest-even).  Any in_dtype / out_dtype pair is accepted.
  *   lse  [B, H, Sq]     fp32, natural log.
  *   d    64 or 128.  scale <= 0 (or NaN) selects 1/sqrt(d).
  *   Skv == 0 gives out = 0 and lse = -inf.  Sq == 0 is a no-op.
@@ -91,7 +94,7 @@ int cpattn_block_fwd(const void* q, const void* k, const void* v, void* out, flo
  * A side with LSE = -inf contributes nothing; two such sides give 0 and -inf.
  *
  *   acc_out [rows, d] fp32, acc_lse [rows] fp32: updated in place.
- *   blk_out [rows, d] blk_dtype (CPATTN_FP32, or CPATTN_BF16 for bf16 partials),
+ *   blk_out [rows, d] blk_dtype (CPATTN_FP32, or CPATTN_BF16 / CPATTN_FP16 for 16-bit partials),
  *   blk_lse [rows] fp32.  rows = B*H*Sq.  d >= 1 with d % 4 == 0.
  * Errors: ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS (blk overlapping acc), ERR_HIP.
  */
@@ -100,7 +103,7 @@ int cpattn_lse_merge(float* acc_out, float* acc_lse, const void* blk_out, const 
 
 /*
  * Bytes of workspace cpattn_ring_fwd needs for these sizes: an fp32
- * [B, H, Sq, d] accumulator when ring_degree > 1 and out_dtype is bf16, else 0.
+ * [B, H, Sq, d] accumulator when ring_degree > 1 and out_dtype is 16-bit, else 0.
  * Returns 0 for invalid sizes as well (cpattn_ring_fwd reports those).
  */
 size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t d, int ring_degree,

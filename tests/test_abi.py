@@ -48,7 +48,8 @@ def test_block_fwd_validation(L):
     assert block(L, d=96) == ERR_SHAPE
     assert b"64 or 128" in L.cpattn_last_error()
     assert block(L, idt=7) == ERR_DTYPE
-    assert block(L, odt=2) == ERR_DTYPE
+    assert block(L, odt=3) == ERR_DTYPE
+    assert block(L, idt=-1) == ERR_DTYPE
     assert block(L, q=NULL) == ERR_NULL
     assert block(L, k=NULL) == ERR_NULL
     assert block(L, lse=NULL) == ERR_NULL
@@ -85,6 +86,7 @@ def test_workspace_bytes(L):
     assert f(1, 24, 2304, 128, 2, 0) == 24 * 2304 * 128 * 4
     assert f(1, 24, 2304, 128, 1, 0) == 0        # one chunk writes out directly
     assert f(1, 24, 2304, 128, 4, 1) == 0        # fp32 out doubles as the accumulator
+    assert f(2, 24, 4096, 64, 2, 2) == 2 * 24 * 4096 * 64 * 4   # fp16 out needs the fp32 accumulator
     assert f(0, 24, 2304, 128, 2, 0) == 0
 
 

@@ -56,3 +56,14 @@ def test_sample_rows():
     assert rows[0] == 0 and rows[-1] == 11193
     assert np.all(np.diff(rows) > 0)
     assert {127, 128, 255, 256}.issubset(set(rows.tolist()))
+
+
+def test_random_bhsd_fp16_is_nearest_even_of_the_same_draw():
+    x, none = W.random_bhsd(3, (2, 3, 5, 8), "fp32")
+    assert none is None
+    v, h = W.random_bhsd(3, (2, 3, 5, 8), "fp16")
+    assert h.dtype == np.float16 and np.array_equal(v, h.astype(np.float32))
+    # nearest representable fp16 of each draw (ties never occur for N(0,1) draws here)
+    err = np.abs(v.astype(np.float64) - x.astype(np.float64))
+    ulp = np.spacing(np.abs(h)).astype(np.float64)
+    assert np.all(err <= 0.5 * ulp)
