@@ -133,12 +133,28 @@ __device__ __forceinline__ u32x4 load8(const void* base, int64_t elem) {
     }
 }
 
-// 16 bytes per lane global -> LDS (global_load_lds_dwordx4): lane l's bytes
-// land at byte 16 l of the 1 KB at `lds`.  Kept out of the templates below:
-// the host pass of hipcc rejects the builtin in a template body instantiated
-// from more than one kernel.
-__device__ __forceinline__ void dma16(const char* g, char* lds) {
-    __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)lds, 16, 0, 0);
+// 16 bytes per lane global -> LDS (buffer_load_dwordx4 ... lds): lane l's
+// bytes come from `rsrc` base + `voff` and land at byte 16 l of the 1 KB at
+// `lds`.  The buffer form takes the wave-uniform base from SGPRs and the lane
+// offset as one 32-bit VGPR, so a DMA costs no VALU address arithmetic.  Kept
+// out of the templates below: the host pass of hipcc rejects LDS-DMA builtins
+// in a template body instantiated from more than one kernel.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (LDS_AS void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Raw buffer descriptor over `p` (bytes from p on are addressable; every
+// offset the kernel forms stays inside the tensor).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const char* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+
+// A wave-uniform pointer, moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
 }
 
 // Per-lane constants of the tile DMA: LDS DMA (global_load_lds_dwordx4)
@@ -173,7 +189,7 @@ template <bool F32, int D, bool IS_V>
 __device__ __forceinline__ void stage_tile(char* smem, int lds_off, const char* src, int t0, int n,
                                            const DmaLane<D, IS_V>& dl, int wave, int lane) {
     using C = Cfg<D>;
-    const char* tile = src + (size_t)t0 * (F32 ? 2 * C::RB : C::RB);
+    const char* tile = uniform_ptr(src + (size_t)t0 * (F32 ? 2 * C::RB : C::RB));
     char* dst0 = smem + lds_off + wave * C::CPW * 1024;
     if (t0 + BN <= n) {
 #pragma unroll
@@ -181,7 +197,7 @@ __device__ __forceinline__ void stage_tile(char* smem, int lds_off, const char* 
             if constexpr (F32) {
                 *reinterpret_cast<u32x4*>(dst0 + i * 1024 + lane * 16) = load8<true>(tile, dl.off[i] / 2);
             } else {
-                dma16(tile + dl.off[i], dst0 + i * 1024);
+                dma16(raw_rsrc(tile), dl.off[i], dst0 + i * 1024);
             }
         }
     } else {
@@ -192,7 +208,7 @@ __device__ __forceinline__ void stage_tile(char* smem, int lds_off, const char* 
             if constexpr (F32) {
                 *reinterpret_cast<u32x4*>(dst0 + i * 1024 + lane * 16) = load8<true>(tile, off / 2);
             } else {
-                dma16(tile + off, dst0 + i * 1024);
+                dma16(raw_rsrc(tile), off, dst0 + i * 1024);
             }
         }
     }
