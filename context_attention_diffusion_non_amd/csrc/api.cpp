@@ -266,7 +266,7 @@ CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, v
 
 CPATTN_EXPORT int cpattn_ulysses_permute(const void* in, void* out, int64_t B, int64_t S_local, int64_t H, int64_t d,
                                          int degree, int group, int direction, int64_t elem_bytes, void* stream) {
-    if (degree < 1) return fail(CPATTN_ERR_DEGREE, "degree must be >= 1 (got %d)", degree);
+    if (degree < 1 || degree > 65535) return fail(CPATTN_ERR_DEGREE, "degree must lie in [1, 65535] (got %d)", degree);
     if (group < -1 || group >= degree) return fail(CPATTN_ERR_DEGREE, "group %d outside [-1, %d)", group, degree);
     if (direction != 0 && direction != 1) return fail(CPATTN_ERR_DTYPE, "direction must be 0 or 1 (got %d)", direction);
     if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)

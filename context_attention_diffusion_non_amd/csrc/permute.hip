@@ -5,21 +5,25 @@
 // that regroup (and of its inverse), a pure copy of d-element rows:
 //   seq -> head:  out[g'][b][h'][r*S_local + s][:] = in[r][b][s][g*H/P + h'][:]
 //   head -> seq:  the inverse map.
-// Rows of whole 16-byte units go through an LDS-tiled transpose (below); other
-// row sizes use a direct copy in units of U bytes where each thread moves UNR
-// units, loads first, then stores.  Index decomposition uses multiply-high
-// division by host-computed magic numbers, so the copy stays memory-bound.
-// Direct grid: x over (b, s, h', unit) of one (rank, group) slice, y = rank r,
-// z = group.
+// Each thread moves UNR units of U bytes (the largest power of two <= 16 that
+// divides a row), loads first, then stores; rows of whole 16-byte units move
+// one unit per thread with non-temporal loads and stores (every byte is
+// touched once, and many small workgroups keep the most bytes in flight).
+// Threads walk the source contiguously; a wave's stores land as whole 128-byte
+// pieces of d-element rows.  Index decomposition uses multiply-high division
+// by host-computed magic numbers, so the copy stays memory-bound.
+// Grid: x over (b, s, h', unit) of one (rank, group) slice, y = rank r,
+// z = group.  Packing q, k and v along B (as one all-to-all buffer would)
+// permutes all three in one launch.
 #include "internal.h"
 
-#include <algorithm>
 
 namespace cpattn {
 namespace {
 
 constexpr int NT = 256;
-constexpr int UNR = 4;
+
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
 
 // n / d for 0 <= n < 2^31 and 1 <= d < 2^31 (round-up multiplier method):
 // l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(m, n) + n) >> l.
@@ -56,18 +60,16 @@ struct PermGeom {
     int direction;
 };
 
-template <int U>
+template <int U, int UNR>
 __global__ __launch_bounds__(NT) void permute_kernel(const char* __restrict__ in, char* __restrict__ out,
                                                      PermGeom g) {
     typedef typename Unit<U>::T T;
     const int64_t r = blockIdx.y;       // sequence shard (source rank)
     const int64_t gi = blockIdx.z;      // group index within this call
     const int64_t grp = g.g0 + gi;
-    const int64_t P = gridDim.y;
     // element-row strides, in units
     const int64_t seq_base = ((r * g.B) * g.S_loc * g.H + grp * g.hpv) * g.uprv;  // in [P,B,S_loc,H,row]
     const int64_t head_base = (gi * g.B * g.hpv * g.S + r * g.S_loc) * g.uprv;    // in [G,B,hp,S,row]
-    (void)P;
 
     T val[UNR];
     int64_t dst[UNR];
@@ -87,102 +89,27 @@ __global__ __launch_bounds__(NT) void permute_kernel(const char* __restrict__ in
         const int64_t head_idx = head_base + (((int64_t)b * g.hpv + hh) * g.S + s) * g.uprv + u;
         const int64_t src = g.direction == 0 ? seq_idx : head_idx;
         dst[j] = g.direction == 0 ? head_idx : seq_idx;
-        val[j] = reinterpret_cast<const T*>(in)[src];
+        if constexpr (U == 16)
+            val[j] = __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(in) + src));
+        else
+            val[j] = reinterpret_cast<const T*>(in)[src];
     }
 #pragma unroll
-    for (int j = 0; j < UNR; ++j)
-        if (ok[j]) reinterpret_cast<T*>(out)[dst[j]] = val[j];
-}
-
-// LDS-tiled variant for rows that are whole 16-byte units.  A workgroup moves
-// TS consecutive tokens of one (rank, batch, group): it reads them as TS runs of
-// hp*row contiguous bytes (sequence layout) into LDS, then writes each head's
-// TS rows as one contiguous run (head layout) -- or the reverse for head ->
-// sequence.  Global accesses are non-temporal: every byte is touched once.
-// LDS holds token s's units at s * (RU + 1) + (h' * upr + u), the one-unit pad
-// per token keeping the strided side of the transpose off a single bank group.
-struct TiledGeom {
-    FastDiv f_ru;      // units per token in the group = hp * upr
-    FastDiv f_upr;     // units per row
-    FastDiv f_tsu;     // TS * upr (one head's rows in a full tile)
-    int64_t B, S_loc, H, S, hp, upr;
-    int TS;
-    int g0;
-};
-
-typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
-
-template <int DIR>
-__global__ __launch_bounds__(NT) void permute_tiled_kernel(const uint4* __restrict__ in, uint4* __restrict__ out,
-                                                           TiledGeom g) {
-    extern __shared__ uint4 tile[];
-    const int64_t r = blockIdx.y;
-    const int64_t gi = blockIdx.z / g.B, b = blockIdx.z % g.B;
-    const int64_t grp = g.g0 + gi;
-    const int64_t s0 = (int64_t)blockIdx.x * g.TS;
-    const uint32_t nt = (uint32_t)min((int64_t)g.TS, g.S_loc - s0);  // tokens in this tile
-    const uint32_t ru = g.f_ru.d, upr = g.f_upr.d, tsu = g.f_tsu.d;
-    const uint32_t n_tok = nt * ru;                  // units, token-major walk
-    const uint32_t n_head = (uint32_t)g.hp * tsu;    // units, head-major walk over a full tile
-    // unit index of token (s0 + s), head h', unit u in each layout
-    const int64_t seq_base = (((r * g.B + b) * g.S_loc + s0) * g.H + grp * g.hp) * g.upr;  // + s*H*upr + h'*upr + u
-    const int64_t head_base = ((gi * g.B + b) * g.hp * g.S + r * g.S_loc + s0) * g.upr;   // + h'*S*upr + s*upr + u
-    const int64_t seq_tok = g.H * g.upr, head_row = g.S * g.upr;
-
-    // token-major position x -> (global unit index in the sequence layout, LDS slot)
-    auto tok = [&](uint32_t x, int64_t& gidx, uint32_t& li) {
-        const uint32_t s = fdiv(x, g.f_ru), rest = x - s * ru;
-        gidx = seq_base + (int64_t)s * seq_tok + rest;
-        li = s * (ru + 1) + rest;
-    };
-    // head-major position x -> (global unit index in the head layout, LDS slot); false past the tile
-    auto head = [&](uint32_t x, int64_t& gidx, uint32_t& li) -> bool {
-        const uint32_t hh = fdiv(x, g.f_tsu), rem = x - hh * tsu;
-        const uint32_t s = fdiv(rem, g.f_upr), u = rem - s * upr;
-        gidx = head_base + (int64_t)hh * head_row + (int64_t)s * g.upr + u;
-        li = s * (ru + 1) + hh * upr + u;
-        return s < nt;
-    };
-
-    // phase 1: global -> LDS, walking the source layout contiguously
-    const uint32_t n1 = DIR == 0 ? n_tok : n_head;
-    for (uint32_t base = threadIdx.x; base < n1; base += NT * UNR) {
-        nt_u32x4 v[UNR];
-        uint32_t li[UNR];
-        bool ok[UNR];
-#pragma unroll
-        for (int j = 0; j < UNR; ++j) {
-            const uint32_t x = base + j * NT;
-            int64_t src = 0;
-            ok[j] = x < n1;
-            if (ok[j]) {
-                if (DIR == 0) tok(x, src, li[j]);
-                else ok[j] = head(x, src, li[j]);
-            }
-            if (ok[j]) v[j] = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(in + src));
-        }
-#pragma unroll
-        for (int j = 0; j < UNR; ++j)
-            if (ok[j]) tile[li[j]] = __builtin_bit_cast(uint4, v[j]);
-    }
-    __syncthreads();
-    // phase 2: LDS -> global, walking the destination layout contiguously
-    const uint32_t n2 = DIR == 0 ? n_head : n_tok;
-    for (uint32_t x = threadIdx.x; x < n2; x += NT) {
-        int64_t dst;
-        uint32_t li;
-        bool ok = true;
-        if (DIR == 0) ok = head(x, dst, li);
-        else tok(x, dst, li);
-        if (ok) __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, tile[li]), reinterpret_cast<nt_u32x4*>(out + dst));
+    for (int j = 0; j < UNR; ++j) {
+        if (!ok[j]) continue;
+        if constexpr (U == 16)
+            __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, val[j]), reinterpret_cast<nt_u32x4*>(out) + dst[j]);
+        else
+            reinterpret_cast<T*>(out)[dst[j]] = val[j];
     }
 }
 
 template <int U>
 hipError_t launch_u(const PermuteArgs& a, const PermGeom& g, int ngroups, hipStream_t stream) {
-    const uint32_t nblk = (g.n_units + NT * UNR - 1) / (NT * UNR);
-    hipLaunchKernelGGL((permute_kernel<U>), dim3(nblk, (unsigned)a.degree, (unsigned)ngroups), dim3(NT), 0, stream,
-                       static_cast<const char*>(a.in), static_cast<char*>(a.out), g);
+    constexpr int UNR = U == 16 ? 1 : 4;
+    const uint32_t nblk = (uint32_t)(((int64_t)g.n_units + NT * UNR - 1) / (NT * UNR));
+    hipLaunchKernelGGL((permute_kernel<U, UNR>), dim3(nblk, (unsigned)a.degree, (unsigned)ngroups), dim3(NT), 0,
+                       stream, static_cast<const char*>(a.in), static_cast<char*>(a.out), g);
     return hipGetLastError();
 }
 
@@ -212,32 +139,6 @@ hipError_t launch_ulysses_permute(const PermuteArgs& a, hipStream_t stream) {
     g.g0 = a.group < 0 ? 0 : a.group;
     g.direction = a.direction;
     const int ngroups = a.group < 0 ? a.degree : 1;
-    // LDS-tiled transpose when rows are whole 16-byte units and a token's group fits in LDS
-    constexpr int64_t kTileBytes = 32768;
-    const int64_t ru = hp * upr;
-    if (U == 16 && (ru + 1) * 16 <= kTileBytes && a.B * ngroups < 65536 && a.degree < 65536) {
-        TiledGeom tg;
-        tg.TS = (int)std::min<int64_t>(8, kTileBytes / ((ru + 1) * 16));
-        tg.f_ru = make_fastdiv((uint32_t)ru);
-        tg.f_upr = make_fastdiv((uint32_t)upr);
-        tg.f_tsu = make_fastdiv((uint32_t)(tg.TS * upr));
-        tg.B = a.B;
-        tg.S_loc = a.S_local;
-        tg.H = a.H;
-        tg.S = a.S_local * a.degree;
-        tg.hp = hp;
-        tg.upr = upr;
-        tg.g0 = a.group < 0 ? 0 : a.group;
-        const size_t lds = (size_t)tg.TS * (ru + 1) * 16;
-        const dim3 grid((unsigned)((a.S_local + tg.TS - 1) / tg.TS), (unsigned)a.degree, (unsigned)(a.B * ngroups));
-        const uint4* in = static_cast<const uint4*>(a.in);
-        uint4* out = static_cast<uint4*>(a.out);
-        if (a.direction == 0)
-            hipLaunchKernelGGL((permute_tiled_kernel<0>), grid, dim3(NT), lds, stream, in, out, tg);
-        else
-            hipLaunchKernelGGL((permute_tiled_kernel<1>), grid, dim3(NT), lds, stream, in, out, tg);
-        return hipGetLastError();
-    }
     switch (U) {
         case 16: return launch_u<16>(a, g, ngroups, stream);
         case 8: return launch_u<8>(a, g, ngroups, stream);

@@ -43,6 +43,12 @@ def _scale(scale: Optional[float]) -> float:
     return 0.0 if scale is None else float(scale)
 
 
+def _shape(t: torch.Tensor, shape, name: str) -> None:
+    """The library takes raw pointers: every buffer is checked against the sizes it is given."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_len: Optional[int] = None,
               scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
@@ -51,13 +57,21 @@ def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_len: Opti
     _dev(q, k, v)
     B, H, Sq, d = q.shape
     kv_ld = k.shape[2]
+    _shape(k, (B, H, kv_ld, d), "k")
+    _shape(v, (B, H, kv_ld, d), "v")
     skv = kv_ld if kv_len is None else int(kv_len)
+    if not 0 <= skv <= kv_ld:
+        raise ValueError(f"kv_len must lie in [0, {kv_ld}]")
     od = out_dtype or q.dtype
     if out is None:
         out = torch.empty((B, H, Sq, d), dtype=od, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     _dev(out, lse)
+    _shape(out, (B, H, Sq, d), "out")
+    _shape(lse, (B, H, Sq), "lse")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
     check(_lib.lib().cpattn_block_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, skv, kv_ld, d,
                                       _scale(scale), _dtype_code(q), _dtype_code(out), _stream(q)))
     return out, lse
@@ -70,6 +84,9 @@ def lse_merge(acc_out: torch.Tensor, acc_lse: torch.Tensor, blk_out: torch.Tenso
         raise TypeError("accumulator and LSE tensors must be float32")
     d = acc_out.shape[-1]
     rows = acc_out.numel() // d if d else 0
+    _shape(blk_out, acc_out.shape, "blk_out")
+    if acc_lse.numel() != rows or blk_lse.numel() != rows:
+        raise ValueError(f"acc_lse and blk_lse must hold {rows} values")
     check(_lib.lib().cpattn_lse_merge(_ptr(acc_out), _ptr(acc_lse), _ptr(blk_out), _ptr(blk_lse), rows, d,
                                       _dtype_code(blk_out), _stream(acc_out)))
 
@@ -87,15 +104,23 @@ def ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int
     _dev(q, k, v)
     B, H, Sq, d = q.shape
     skv = k.shape[2]
+    _shape(k, (B, H, skv, d), "k")
+    _shape(v, (B, H, skv, d), "v")
     od = out_dtype or q.dtype
     if out is None:
         out = torch.empty((B, H, Sq, d), dtype=od, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     _dev(out, lse)
+    _shape(out, (B, H, Sq, d), "out")
+    _shape(lse, (B, H, Sq), "lse")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
     need = int(_lib.lib().cpattn_ring_fwd_workspace_bytes(B, H, Sq, d, ring_degree, _dtype_code(out)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lens = None
     if chunk_lens is not None:
@@ -132,13 +157,17 @@ def ulysses_permute(x: torch.Tensor, degree: int, group: int = 0, direction: int
         if group >= 0:
             B, hp, S, d = x.shape
         else:
-            _, B, hp, S, d = x.shape
+            G, B, hp, S, d = x.shape
+            if G != degree:
+                raise ValueError("x.shape[0] must equal degree for group -1")
         if degree < 1 or S % degree:
             raise ValueError("S must divide by degree")
         S_loc, H = S // degree, hp * degree
+        shape = (degree, B, S_loc, H, d)
         if out is None:
-            out = torch.zeros((degree, B, S_loc, H, d), dtype=x.dtype, device=x.device)
+            out = torch.zeros(shape, dtype=x.dtype, device=x.device)
     _dev(out)
+    _shape(out, shape, "out")
     if out.dtype != x.dtype:
         raise TypeError("out must have x's dtype")
     check(_lib.lib().cpattn_ulysses_permute(_ptr(x), _ptr(out), B, S_loc, H, d, int(degree), int(group),

@@ -95,7 +95,7 @@ int cpattn_block_fwd(const void* q, const void* k, const void* v, void* out, flo
  *
  *   acc_out [rows, d] fp32, acc_lse [rows] fp32: updated in place.
  *   blk_out [rows, d] blk_dtype (CPATTN_FP32, or CPATTN_BF16 / CPATTN_FP16 for 16-bit partials),
- *   blk_lse [rows] fp32.  rows = B*H*Sq.  d >= 1 with d % 4 == 0.
+ *   blk_lse [rows] fp32.  rows = B*H*Sq.  d a power of two in [4, 256].
  * Errors: ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIAS (blk overlapping acc), ERR_HIP.
  */
 int cpattn_lse_merge(float* acc_out, float* acc_lse, const void* blk_out, const float* blk_lse,
@@ -156,7 +156,7 @@ int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, floa
  *     tensor, `out` the [P, B, S_local, H, d] tensor, of which only the heads of
  *     the given group(s) are written.
  *   elem_bytes: 1, 2, 4 or 8 (bf16 = 2).  The copy is bit-exact.
- * Errors: ERR_NULL, ERR_SHAPE, ERR_DEGREE (degree < 1 or group outside [-1, P)),
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_DEGREE (degree outside [1, 65535] or group outside [-1, P)),
  *         ERR_INDIVISIBLE (H % P), ERR_DTYPE (elem_bytes or direction), ERR_ALIAS
  *         (out overlapping in), ERR_HIP.
  */

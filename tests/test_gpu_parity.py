@@ -284,3 +284,22 @@ def test_error_path_launches_nothing():
     assert e.value.name == "CPATTN_ERR_INDIVISIBLE"
     torch.cuda.synchronize()
     assert torch.all(out == 7.0) and torch.all(lse == 7.0)
+
+
+def test_binding_rejects_wrong_buffer_shapes():
+    """The C ABI takes raw pointers, so the binding checks every buffer's shape
+    before a call: a too-small output must never reach a kernel."""
+    _, q = rand_bf16(97, (1, 2, 64, 128))
+    _, k = rand_bf16(98, (1, 2, 80, 128))
+    with pytest.raises(ValueError):
+        ops.block_fwd(q, k, k[:, :, :40].contiguous())
+    with pytest.raises(ValueError):
+        ops.block_fwd(q, k, k, out=torch.empty(1, 2, 32, 128, device=DEV))
+    with pytest.raises(ValueError):
+        ops.ring_fwd(q, k, k, 2, lse=torch.empty(1, 2, 63, device=DEV))
+    x = torch.zeros(2, 1, 16, 4, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        ops.ulysses_permute(x, 2, 0, 0, out=torch.empty(1, 2, 16, 64, dtype=torch.bfloat16, device=DEV))
+    acc = torch.zeros(10, 64, device=DEV)
+    with pytest.raises(ValueError):
+        ops.lse_merge(acc, torch.zeros(9, device=DEV), acc.clone(), torch.zeros(10, device=DEV))
