@@ -22,7 +22,10 @@ What it computes, plainly and slowly, in float64 numpy:
   Attention and Ring Anything Attention sections);
 * ``ulysses_seq_to_head`` / ``ulysses_head_to_seq`` -- the Ulysses regroup from
   "every head for a slice of tokens" to "every token for a slice of heads" and
-  back ("Context parallelism" page, Ulysses Attention section).
+  back ("Context parallelism" page, Ulysses Attention section);
+* ``unified_rank_share`` / ``unified_all_ranks`` -- Unified attention on a
+  ring x Ulysses grid: the regroup, the ring over the regrouped segments, and
+  the reverse regroup ("Context parallelism" page, Unified Attention section).
 
 Every function is pinned by the CPU tests in ``tests/test_oracle_pins.py``
 (closed forms, invariants, brute force and a library cross-check).
@@ -31,8 +34,9 @@ from .attention import attention, attention_rows
 from .merge import lse_merge, empty_partial
 from .ring import ring_attention
 from .permute import ulysses_seq_to_head, ulysses_head_to_seq
+from .unified import unified_rank_share, unified_all_ranks
 
 __all__ = [
     "attention", "attention_rows", "lse_merge", "empty_partial", "ring_attention",
-    "ulysses_seq_to_head", "ulysses_head_to_seq",
+    "ulysses_seq_to_head", "ulysses_head_to_seq", "unified_rank_share", "unified_all_ranks",
 ]

@@ -366,3 +366,65 @@ def check_permute_is_bshd_to_bhsd(seq_to_head):
         for h in range(3):
             for s in range(7):
                 assert np.array_equal(out[b, h, s], x[0, b, s, h])
+
+
+# --------------------------------------------------------------------------
+# unified (Ulysses x Ring)
+# --------------------------------------------------------------------------
+
+def _torch_sdpa_bshd(q, k, v):
+    """Unsplit attention of full-sequence [B, S, H, d] tensors by torch's CPU SDPA in
+    float64 (a library routine), returned as [B, S, H, d] and the LSE [B, S, H]."""
+    import torch
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(np.transpose(x, (0, 2, 1, 3)))) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).numpy()
+    d = q.shape[-1]
+    lse = torch.logsumexp(qt @ kt.transpose(-1, -2) / math.sqrt(d), dim=-1).numpy()
+    return np.transpose(out, (0, 2, 1, 3)), np.transpose(lse, (0, 2, 1))
+
+
+def check_unified_equals_unsplit(unified_all, R, U, seed=50, B=2, S_loc=3, H_per=2, d=4):
+    """Every rank's share on a ring_degree x ulysses_degree grid, regrouped back by
+    token, equals unsplit attention of the whole sequence (torch SDPA, fp64):
+    the composition the pages describe loses nothing and reorders nothing."""
+    r = _rng(seed + 7 * R + U)
+    W, H = R * U, H_per * U
+    full = [r.standard_normal((B, W * S_loc, H, d)) for _ in range(3)]
+    shards = [np.ascontiguousarray(x.reshape(B, W, S_loc, H, d).transpose(1, 0, 2, 3, 4)) for x in full]
+    out, lse = unified_all(*shards, R, U)
+    ref_out, ref_lse = _torch_sdpa_bshd(*full)
+    ref_out = ref_out.reshape(B, W, S_loc, H, d).transpose(1, 0, 2, 3, 4)
+    ref_lse = ref_lse.reshape(B, W, S_loc, H).transpose(1, 0, 2, 3)
+    assert out.shape == ref_out.shape and lse.shape == ref_lse.shape
+    assert np.abs(out - ref_out).max() < 1e-12, f"unified {R}x{U} differs from unsplit attention"
+    assert np.abs(lse - ref_lse).max() < 1e-12, f"unified {R}x{U} lse differs from unsplit"
+
+
+def check_unified_share_rows(unified_share, R=2, U=2, seed=60, B=1, S_loc=2, H_per=1, d=4):
+    """One rank's share before the reverse regroup is attention of ITS Ulysses
+    group's tokens (segment ring_rank) for ITS head group against every token:
+    row by row against a pure-Python brute force."""
+    r = _rng(seed)
+    W, H = R * U, H_per * U
+    full = [r.standard_normal((B, W * S_loc, H, d)) for _ in range(3)]
+    shards = [np.ascontiguousarray(x.reshape(B, W, S_loc, H, d).transpose(1, 0, 2, 3, 4)) for x in full]
+    q, k, v = full
+    S = W * S_loc
+    for rho in range(R):
+        for u in range(U):
+            out, lse = unified_share(*shards, R, U, rho, u)
+            assert out.shape == (B, H_per, U * S_loc, d)
+            for b in range(B):
+                for hh in range(H_per):
+                    h = u * H_per + hh
+                    for i in range(U * S_loc):
+                        t = rho * U * S_loc + i
+                        sc = [math.fsum(q[b, t, h, e] * k[b, j, h, e] for e in range(d)) / math.sqrt(d)
+                              for j in range(S)]
+                        m = max(sc)
+                        w = [math.exp(s - m) for s in sc]
+                        z = math.fsum(w)
+                        for e in range(d):
+                            ref = math.fsum(w[j] * v[b, j, h, e] for j in range(S)) / z
+                            assert abs(out[b, hh, i, e] - ref) < 1e-12
+                        assert abs(lse[b, hh, i] - (m + math.log(z))) < 1e-12

@@ -191,3 +191,66 @@ def test_permute_mutant_is_caught(mut):
         return mut(x, degree, group)
     with pytest.raises(AssertionError):
         pins.check_permute_provenance(wrapped)
+
+
+# --- unified: wrong mesh order, ring order not starting at the own segment,
+# reverse regroup into the wrong Ulysses group ---
+
+def mu_mesh_transposed(q, k, v, R, U, ring_rank, ulysses_rank, scale=None):
+    """Ulysses group taken as every R-th shard (rank = ulysses_rank * R + ring_rank)."""
+    W = R * U
+    perm = [u * R + rho for rho in range(R) for u in range(U)]
+    return oracle.unified_rank_share(q[perm], k[perm], v[perm], R, U, ring_rank, ulysses_rank, scale)
+
+
+def mu_query_from_group_zero(q, k, v, R, U, ring_rank, ulysses_rank, scale=None):
+    """Queries always taken from the first Ulysses group's segment."""
+    qq = np.array(q, copy=True)
+    qq[ring_rank * U:(ring_rank + 1) * U] = q[0:U]
+    return oracle.unified_rank_share(qq, k, v, R, U, ring_rank, ulysses_rank, scale)
+
+
+def mu_heads_of_next_group(q, k, v, R, U, ring_rank, ulysses_rank, scale=None):
+    """Keys and values of the wrong head group."""
+    out_q = oracle.unified_rank_share(q, k, v, R, U, ring_rank, ulysses_rank, scale)
+    if U == 1:
+        return out_q
+    kk = np.roll(k, -(k.shape[3] // U), axis=3)
+    vv = np.roll(v, -(v.shape[3] // U), axis=3)
+    return oracle.unified_rank_share(q, kk, vv, R, U, ring_rank, ulysses_rank, scale)
+
+
+@pytest.mark.parametrize("mut", [mu_mesh_transposed, mu_query_from_group_zero, mu_heads_of_next_group],
+                         ids=lambda f: f.__name__)
+def test_unified_mutant_is_caught(mut):
+    def all_ranks(q, k, v, R, U):
+        W, B, S_loc, H, d = q.shape
+        out = np.zeros((W, B, S_loc, H, d))
+        lse = np.zeros((W, B, S_loc, H))
+        for rho in range(R):
+            shares = [mut(q, k, v, R, U, rho, u) for u in range(U)]
+            o = np.stack([s[0] for s in shares])
+            l = np.stack([s[1] for s in shares])[..., None]
+            out[rho * U:(rho + 1) * U] = oracle.ulysses_head_to_seq(o, U, -1)
+            lse[rho * U:(rho + 1) * U] = oracle.ulysses_head_to_seq(l, U, -1)[..., 0]
+        return out, lse
+    caught = False
+    for R, U in [(2, 2), (3, 2)]:
+        try:
+            pins.check_unified_equals_unsplit(all_ranks, R, U)
+        except AssertionError:
+            caught = True
+    try:
+        pins.check_unified_share_rows(mut)
+    except AssertionError:
+        caught = True
+    assert caught, f"{mut.__name__} passed every unified pin"
+
+
+def test_unified_reverse_regroup_mutant_is_caught():
+    """Reverse regroup writing each rank's heads into the neighbouring Ulysses group."""
+    def all_ranks(q, k, v, R, U):
+        out, lse = oracle.unified_all_ranks(q, k, v, R, U)
+        return np.roll(out, U, axis=0), np.roll(lse, U, axis=0)
+    with pytest.raises(AssertionError):
+        pins.check_unified_equals_unsplit(all_ranks, 2, 2)

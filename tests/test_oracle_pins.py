@@ -107,3 +107,12 @@ def test_attention_rows_are_independent():
     full_o, full_l = oracle.attention(q, k, v)
     o, l = oracle.attention_rows(q, k, v, rows)
     assert np.array_equal(o, full_o[:, rows]) and np.array_equal(l, full_l[:, rows])
+
+
+@pytest.mark.parametrize("R,U", [(1, 2), (2, 1), (2, 2), (2, 3), (3, 2), (1, 1)])
+def test_unified_equals_unsplit(R, U):
+    pins.check_unified_equals_unsplit(oracle.unified_all_ranks, R, U)
+
+
+def test_unified_share_rows_brute_force():
+    pins.check_unified_share_rows(oracle.unified_rank_share)
