@@ -37,6 +37,11 @@ _SIGNATURES = {
                                         ctypes.c_int, _vp]),
     "cpattn_ulysses_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, _i64, _vp]),
+    "cpattn_unified_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp,
+                                           ctypes.c_size_t, ctypes.c_int, ctypes.c_int, _vp]),
+    "cpattn_unified_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                              ctypes.c_int, ctypes.c_int]),
     "cpattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "cpattn_last_error": (ctypes.c_char_p, []),
     "cpattn_version": (ctypes.c_int, []),

@@ -125,6 +125,44 @@ cpattn::AttnArgs make_args(const void* q, const void* k, const void* v, void* ou
     return a;
 }
 
+// The ring loop after validation: chunk 0 stores its partial into the fp32
+// accumulator (the output itself when it is fp32 or when there is a single
+// chunk, else `acc_ws`), later chunks LSE-merge into it in their epilogue, and
+// the last one writes `out`.  Chunks are `chunk_lens` (NULL: equal lengths).
+int ring_launch(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H, int64_t Sq,
+                int64_t Skv, int64_t d, float scale, int ring_degree, const int64_t* chunk_lens, float* acc_ws,
+                int in_dtype, int out_dtype, hipStream_t s) {
+    const size_t esz = dtype_bytes(in_dtype);
+    const bool acc_is_out = ring_degree == 1 || out_dtype == CPATTN_FP32;
+    float* acc = acc_is_out ? static_cast<float*>(out) : acc_ws;
+    int64_t off = 0;
+    for (int c_i = 0; c_i < ring_degree; ++c_i) {
+        const int64_t len = chunk_lens ? chunk_lens[c_i] : Skv / ring_degree;
+        const char* kc = static_cast<const char*>(k) + (size_t)off * d * esz;
+        const char* vc = static_cast<const char*>(v) + (size_t)off * d * esz;
+        cpattn::AttnArgs a = make_args(q, kc, vc, nullptr, lse, B, H, Sq, len, Skv, d, scale, in_dtype, out_dtype);
+        const bool last = c_i == ring_degree - 1;
+        if (c_i == 0) {
+            a.mode = cpattn::EPI_STORE;
+        } else {
+            a.mode = cpattn::EPI_MERGE;
+            a.acc_in = acc;
+            a.lse_in = lse;
+        }
+        if (last) {
+            a.out = out;
+            a.out_dtype = out_dtype;
+        } else {
+            a.out = acc;
+            a.out_dtype = cpattn::DT_F32;
+        }
+        const hipError_t e = cpattn::launch_attn_fwd(a, s);
+        if (e != hipSuccess) return hip_fail(e, "attention kernel launch (ring chunk)");
+        off += len;
+    }
+    return CPATTN_OK;
+}
+
 }  // namespace
 
 CPATTN_EXPORT int cpattn_version(void) { return 100; }
@@ -229,39 +267,8 @@ CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, v
     }
     if (Sq == 0) return CPATTN_OK;
 
-    // Plan: chunk 0 stores its partial into the fp32 accumulator (the output
-    // itself when it is fp32 or when there is a single chunk), later chunks
-    // LSE-merge into it in their epilogue, and the last one writes `out`.
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t esz = dtype_bytes(in_dtype);
-    const bool acc_is_out = ring_degree == 1 || out_dtype == CPATTN_FP32;
-    float* acc = acc_is_out ? static_cast<float*>(out) : static_cast<float*>(workspace);
-    int64_t off = 0;
-    for (int c_i = 0; c_i < ring_degree; ++c_i) {
-        const int64_t len = chunk_lens ? chunk_lens[c_i] : Skv / ring_degree;
-        const char* kc = static_cast<const char*>(k) + (size_t)off * d * esz;
-        const char* vc = static_cast<const char*>(v) + (size_t)off * d * esz;
-        cpattn::AttnArgs a = make_args(q, kc, vc, nullptr, lse, B, H, Sq, len, Skv, d, scale, in_dtype, out_dtype);
-        const bool last = c_i == ring_degree - 1;
-        if (c_i == 0) {
-            a.mode = cpattn::EPI_STORE;
-        } else {
-            a.mode = cpattn::EPI_MERGE;
-            a.acc_in = acc;
-            a.lse_in = lse;
-        }
-        if (last) {
-            a.out = out;
-            a.out_dtype = out_dtype;
-        } else {
-            a.out = acc;
-            a.out_dtype = cpattn::DT_F32;
-        }
-        const hipError_t e = cpattn::launch_attn_fwd(a, s);
-        if (e != hipSuccess) return hip_fail(e, "attention kernel launch (ring chunk)");
-        off += len;
-    }
-    return CPATTN_OK;
+    return ring_launch(q, k, v, out, lse, B, H, Sq, Skv, d, scale, ring_degree, chunk_lens,
+                       static_cast<float*>(workspace), in_dtype, out_dtype, static_cast<hipStream_t>(stream));
 }
 
 CPATTN_EXPORT int cpattn_ulysses_permute(const void* in, void* out, int64_t B, int64_t S_local, int64_t H, int64_t d,
@@ -289,8 +296,117 @@ CPATTN_EXPORT int cpattn_ulysses_permute(const void* in, void* out, int64_t B, i
     while (U > 1 && row_bytes % U != 0) U >>= 1;
     if ((B * S_local * (H / degree) * (row_bytes / U)) >= (int64_t(1) << 31))
         return fail(CPATTN_ERR_SHAPE, "one (rank, group) slice exceeds 2^31 copy units");
-    cpattn::PermuteArgs a{in, out, B, S_local, H, d, degree, group, direction, elem_bytes};
+    cpattn::PermuteArgs a{in, out, B, S_local, H, d, degree, group, direction, elem_bytes, degree, 0};
     const hipError_t e = cpattn::launch_ulysses_permute(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
     return CPATTN_OK;
+}
+
+namespace {
+
+// Workspace layout of cpattn_unified_fwd: the regrouped q (the rank's Ulysses
+// group's tokens, its head group), k and v (every token of the grid, its head
+// group, in its ring order) and the ring's fp32 accumulator; 256-byte aligned.
+struct UnifiedPlan {
+    int64_t hq, s_seg, s_all;
+    size_t q_off, k_off, v_off, acc_off, total;
+    bool ok;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+UnifiedPlan unified_plan(int64_t B, int64_t S_local, int64_t H, int64_t d, int R, int U, int in_dtype, int out_dtype) {
+    UnifiedPlan p{};
+    p.ok = false;
+    if (B < 1 || H < 1 || S_local < 0 || d < 1 || R < 1 || U < 1 || H % U != 0) return p;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return p;
+    p.hq = H / U;
+    int64_t seg = S_local, all = S_local;
+    if (!mul_ok(seg, U) || !mul_ok(all, U) || !mul_ok(all, R)) return p;
+    p.s_seg = seg;
+    p.s_all = all;
+    int64_t qn = B, kn = B, an = B;
+    if (!mul_ok(qn, p.hq) || !mul_ok(qn, seg) || !mul_ok(qn, d) || !mul_ok(qn, (int64_t)dtype_bytes(in_dtype)) ||
+        !mul_ok(kn, p.hq) || !mul_ok(kn, all) || !mul_ok(kn, d) || !mul_ok(kn, (int64_t)dtype_bytes(in_dtype)) ||
+        !mul_ok(an, p.hq) || !mul_ok(an, seg) || !mul_ok(an, d) || !mul_ok(an, 4))
+        return p;
+    const bool need_acc = R > 1 && out_dtype != CPATTN_FP32;
+    p.q_off = 0;
+    p.k_off = align256((size_t)qn);
+    p.v_off = p.k_off + align256((size_t)kn);
+    p.acc_off = p.v_off + align256((size_t)kn);
+    p.total = p.acc_off + (need_acc ? align256((size_t)an) : 0);
+    p.ok = true;
+    return p;
+}
+
+}  // namespace
+
+CPATTN_EXPORT size_t cpattn_unified_fwd_workspace_bytes(int64_t B, int64_t S_local, int64_t H, int64_t d,
+                                                        int ring_degree, int ulysses_degree, int in_dtype,
+                                                        int out_dtype) {
+    const UnifiedPlan p = unified_plan(B, S_local, H, d, ring_degree, ulysses_degree, in_dtype, out_dtype);
+    return p.ok ? p.total : 0;
+}
+
+CPATTN_EXPORT int cpattn_unified_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                     int64_t S_local, int64_t H, int64_t d, float scale, int ring_degree,
+                                     int ulysses_degree, int ring_rank, int ulysses_rank, void* workspace,
+                                     size_t workspace_bytes, int in_dtype, int out_dtype, void* stream) {
+    const int R = ring_degree, U = ulysses_degree;
+    if (R < 1 || U < 1 || (int64_t)R * U > 65535)
+        return fail(CPATTN_ERR_DEGREE, "ring_degree=%d, ulysses_degree=%d: each >= 1, product <= 65535", R, U);
+    if (ring_rank < 0 || ring_rank >= R || ulysses_rank < 0 || ulysses_rank >= U)
+        return fail(CPATTN_ERR_DEGREE, "rank (%d, %d) outside the %d x %d grid", ring_rank, ulysses_rank, R, U);
+    if (B < 1 || H < 1 || S_local < 0) return fail(CPATTN_ERR_SHAPE, "invalid unified shape");
+    if (d != 64 && d != 128) return fail(CPATTN_ERR_SHAPE, "head dim d must be 64 or 128 (got %lld)", (long long)d);
+    if (H % U != 0) return fail(CPATTN_ERR_INDIVISIBLE, "H=%lld is not divisible by ulysses_degree=%d", (long long)H, U);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(CPATTN_ERR_DTYPE, "unsupported dtype");
+    const UnifiedPlan p = unified_plan(B, S_local, H, d, R, U, in_dtype, out_dtype);
+    if (!p.ok) return fail(CPATTN_ERR_SHAPE, "unified sizes overflow");
+    const int64_t W = (int64_t)R * U;
+    int64_t shard_bytes = W;
+    if (!mul_ok(shard_bytes, B) || !mul_ok(shard_bytes, S_local) || !mul_ok(shard_bytes, H) || !mul_ok(shard_bytes, d) ||
+        !mul_ok(shard_bytes, (int64_t)dtype_bytes(in_dtype)))
+        return fail(CPATTN_ERR_SHAPE, "unified sizes overflow");
+    const int64_t row_bytes = d * (int64_t)dtype_bytes(in_dtype);
+    if (B * S_local * p.hq * (row_bytes / 16) >= (int64_t(1) << 31))
+        return fail(CPATTN_ERR_SHAPE, "one (shard, group) slice exceeds 2^31 copy units");
+    if (S_local == 0) return CPATTN_OK;
+    if (!q || !k || !v || !out || !lse) return fail(CPATTN_ERR_NULL, "a unified pointer is NULL");
+    if (workspace == nullptr || workspace_bytes < p.total)
+        return fail(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", p.total, workspace_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+        return fail(CPATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    const void* ins[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(workspace, p.total, ins[i], (size_t)shard_bytes)) return fail(CPATTN_ERR_ALIAS, "workspace overlaps an input");
+    // the regrouped tensors play q, k, v for the attention checks (sizes, out/lse aliasing)
+    AttnCheck c;
+    int st = check_attn(ws + p.q_off, ws + p.k_off, ws + p.v_off, out, lse, B, p.hq, p.s_seg, p.s_all, p.s_all, d,
+                        in_dtype, out_dtype, c);
+    if (st != CPATTN_OK) return st;
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(out, c.out_bytes, ins[i], (size_t)shard_bytes) || overlaps(lse, c.lse_bytes, ins[i], (size_t)shard_bytes))
+            return fail(CPATTN_ERR_ALIAS, "out/lse overlap an input");
+    if (p.total > p.acc_off && (overlaps(ws + p.acc_off, p.total - p.acc_off, out, c.out_bytes) ||
+                                overlaps(ws + p.acc_off, p.total - p.acc_off, lse, c.lse_bytes)))
+        return fail(CPATTN_ERR_ALIAS, "workspace overlaps an output");
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t eb = (int64_t)dtype_bytes(in_dtype);
+    // q: the U shards of the rank's Ulysses group -> every token of its segment, head group ulysses_rank
+    const char* q_grp = static_cast<const char*>(q) + (size_t)ring_rank * U * B * S_local * H * d * eb;
+    cpattn::PermuteArgs pq{q_grp, ws + p.q_off, B, S_local, H, d, U, ulysses_rank, 0, eb, U, 0};
+    // k, v: all W shards -> every token, head group ulysses_rank, segments in ring order from the rank's own
+    cpattn::PermuteArgs pk{k, ws + p.k_off, B, S_local, H, d, (int)W, ulysses_rank, 0, eb, U, ring_rank * U};
+    cpattn::PermuteArgs pv{v, ws + p.v_off, B, S_local, H, d, (int)W, ulysses_rank, 0, eb, U, ring_rank * U};
+    const cpattn::PermuteArgs* perms[3] = {&pq, &pk, &pv};
+    for (int i = 0; i < 3; ++i) {
+        const hipError_t e = cpattn::launch_ulysses_permute(*perms[i], s);
+        if (e != hipSuccess) return hip_fail(e, "unified regroup launch");
+    }
+    return ring_launch(ws + p.q_off, ws + p.k_off, ws + p.v_off, out, lse, B, p.hq, p.s_seg, p.s_all, d, scale, R,
+                       nullptr, reinterpret_cast<float*>(ws + p.acc_off), in_dtype, out_dtype, s);
 }

@@ -56,10 +56,12 @@ struct PermuteArgs {
     const void* in;
     void* out;
     int64_t B, S_local, H, d;
-    int degree;
-    int group;             // -1: all groups
+    int degree;            // sequence shards P
+    int group;             // head group to move, -1: all groups
     int direction;         // 0 seq->head, 1 head->seq
     int64_t elem_bytes;
+    int groups;            // head groups G (H % G == 0); the Ulysses permute has G == P
+    int rot;               // seq->head: output block r takes shard (r + rot) % P
 };
 
 hipError_t launch_ulysses_permute(const PermuteArgs& a, hipStream_t stream);

@@ -5,6 +5,10 @@
 // that regroup (and of its inverse), a pure copy of d-element rows:
 //   seq -> head:  out[g'][b][h'][r*S_local + s][:] = in[r][b][s][g*H/P + h'][:]
 //   head -> seq:  the inverse map.
+// Internally the shard count P and the head-group count G may differ, and the
+// seq -> head direction may rotate the shards (output block r from shard
+// (r + rot) % P): Unified attention regroups the K/V shards of a whole ring x
+// Ulysses grid into one head group, in the ring order of one rank.
 // Each thread moves UNR units of U bytes (the largest power of two <= 16 that
 // divides a row), loads first, then stores; rows of whole 16-byte units move
 // one unit per thread with non-temporal loads and stores (every byte is
@@ -58,17 +62,20 @@ struct PermGeom {
     int64_t B, S_loc, H, S, hpv, uprv;
     int g0;            // first group
     int direction;
+    int P;             // shards
+    int rot;           // seq -> head shard rotation
 };
 
 template <int U, int UNR>
 __global__ __launch_bounds__(NT) void permute_kernel(const char* __restrict__ in, char* __restrict__ out,
                                                      PermGeom g) {
     typedef typename Unit<U>::T T;
-    const int64_t r = blockIdx.y;       // sequence shard (source rank)
+    const int64_t r = blockIdx.y;       // sequence block of the head layout
     const int64_t gi = blockIdx.z;      // group index within this call
     const int64_t grp = g.g0 + gi;
+    const int64_t shard = (r + g.rot) % g.P;  // sequence shard it comes from (rot = 0 for head -> seq)
     // element-row strides, in units
-    const int64_t seq_base = ((r * g.B) * g.S_loc * g.H + grp * g.hpv) * g.uprv;  // in [P,B,S_loc,H,row]
+    const int64_t seq_base = ((shard * g.B) * g.S_loc * g.H + grp * g.hpv) * g.uprv;  // in [P,B,S_loc,H,row]
     const int64_t head_base = (gi * g.B * g.hpv * g.S + r * g.S_loc) * g.uprv;    // in [G,B,hp,S,row]
 
     T val[UNR];
@@ -120,7 +127,7 @@ hipError_t launch_ulysses_permute(const PermuteArgs& a, hipStream_t stream) {
     int U = 16;
     while (U > 1 && row_bytes % U != 0) U >>= 1;
     const int64_t upr = row_bytes / U;
-    const int64_t hp = a.H / a.degree;
+    const int64_t hp = a.H / a.groups;
     const int64_t n_units = a.B * a.S_local * hp * upr;
     if (n_units <= 0) return hipSuccess;
     if (n_units >= (int64_t(1) << 31) || upr >= (int64_t(1) << 31) || a.S_local >= (int64_t(1) << 31))
@@ -138,7 +145,9 @@ hipError_t launch_ulysses_permute(const PermuteArgs& a, hipStream_t stream) {
     g.uprv = upr;
     g.g0 = a.group < 0 ? 0 : a.group;
     g.direction = a.direction;
-    const int ngroups = a.group < 0 ? a.degree : 1;
+    g.P = a.degree;
+    g.rot = a.direction == 0 ? a.rot : 0;
+    const int ngroups = a.group < 0 ? a.groups : 1;
     switch (U) {
         case 16: return launch_u<16>(a, g, ngroups, stream);
         case 8: return launch_u<8>(a, g, ngroups, stream);

@@ -175,5 +175,54 @@ def ulysses_permute(x: torch.Tensor, degree: int, group: int = 0, direction: int
     return out
 
 
-__all__ = ["block_fwd", "lse_merge", "ring_fwd", "ring_fwd_workspace_bytes", "ulysses_permute", "CpattnError",
-           "BF16", "FP16", "FP32"]
+def unified_fwd_workspace_bytes(B: int, S_local: int, H: int, d: int, ring_degree: int, ulysses_degree: int,
+                                in_dtype: torch.dtype, out_dtype: torch.dtype) -> int:
+    return int(_lib.lib().cpattn_unified_fwd_workspace_bytes(B, S_local, H, d, ring_degree, ulysses_degree,
+                                                              _DT[in_dtype], _DT[out_dtype]))
+
+
+def unified_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int, ulysses_degree: int,
+                ring_rank: int, ulysses_rank: int, *, scale: Optional[float] = None,
+                out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cpattn_unified_fwd: rank (ring_rank, ulysses_rank)'s share of Unified attention.
+
+    q, k, v: [W, B, S_local, H, d] sequence shards of all W = ring_degree * ulysses_degree ranks.
+    Returns out [B, H/U, U*S_local, d] and lse [B, H/U, U*S_local] (head-sharded, before the
+    reverse regroup, which is ``ulysses_permute(..., direction=1)`` over a Ulysses group's outputs).
+    """
+    _dev(q, k, v)
+    W, B, S_loc, H, d = q.shape
+    _shape(k, q.shape, "k")
+    _shape(v, q.shape, "v")
+    if ring_degree < 1 or ulysses_degree < 1 or W != ring_degree * ulysses_degree:
+        raise ValueError("q.shape[0] must equal ring_degree * ulysses_degree")
+    if H % ulysses_degree:
+        raise ValueError("H must divide by ulysses_degree")
+    hq, seg = H // ulysses_degree, ulysses_degree * S_loc
+    od = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, hq, seg, d), dtype=od, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, hq, seg), dtype=torch.float32, device=q.device)
+    _dev(out, lse)
+    _shape(out, (B, hq, seg, d), "out")
+    _shape(lse, (B, hq, seg), "lse")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    need = int(_lib.lib().cpattn_unified_fwd_workspace_bytes(B, S_loc, H, d, ring_degree, ulysses_degree,
+                                                              _dtype_code(q), _dtype_code(out)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _dev(workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(_lib.lib().cpattn_unified_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, S_loc, H, d,
+                                        _scale(scale), int(ring_degree), int(ulysses_degree), int(ring_rank),
+                                        int(ulysses_rank), _ptr(workspace), ws_bytes, _dtype_code(q),
+                                        _dtype_code(out), _stream(q)))
+    return out, lse
+
+
+__all__ = ["block_fwd", "lse_merge", "ring_fwd", "ring_fwd_workspace_bytes", "ulysses_permute", "unified_fwd",
+           "unified_fwd_workspace_bytes", "CpattnError", "BF16", "FP16", "FP32"]

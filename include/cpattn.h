@@ -163,6 +163,46 @@ int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, floa
 int cpattn_ulysses_permute(const void* in, void* out, int64_t B, int64_t S_local, int64_t H, int64_t d,
                            int degree, int group, int direction, int64_t elem_bytes, void* stream);
 
+/*
+ * cpattn_unified_fwd -- one rank's share of Unified attention on a
+ * ring_degree x ulysses_degree grid of ranks.
+ *
+ * "Context parallelism" page, Unified Attention: an all-to-all redistributes
+ * heads and tokens, Ring Attention runs on the result, and the all-to-all is
+ * reversed; every rank belongs to one Ulysses group and one ring group.  With
+ * the grid's dimensions ordered (ring, Ulysses) as in the ParaAttention README
+ * example, rank w = ring_rank * ulysses_degree + ulysses_rank; its Ulysses
+ * group is the ulysses_degree ranks sharing its ring_rank (consecutive
+ * sequence shards) and its ring group the ring_degree ranks sharing its
+ * ulysses_rank.  This call computes, for rank (ring_rank, ulysses_rank):
+ *   1. the Ulysses regroup of q inside its Ulysses group -> every token of
+ *      segment ring_rank (U * S_local tokens) for head group ulysses_rank, and
+ *      of k and v in every Ulysses group -> every token of the grid for that
+ *      head group, segments in the rank's ring order (its own first);
+ *   2. the ring loop over the ring_degree segments (cpattn_ring_fwd numerics).
+ * The reverse regroup that returns outputs by token is cpattn_ulysses_permute
+ * (direction 1) over the U outputs of a Ulysses group.
+ *
+ *   q, k, v  [W, B, S_local, H, d] in_dtype, W = ring_degree * ulysses_degree:
+ *            the sequence shards of every rank stacked (shard w holds tokens
+ *            [w * S_local, (w + 1) * S_local)), as the all-to-all consumes them.
+ *   out  [B, H / U, U * S_local, d] out_dtype;  lse [B, H / U, U * S_local] fp32.
+ *   workspace: cpattn_unified_fwd_workspace_bytes(...) bytes, 256-byte aligned:
+ *            the regrouped q, k, v and the ring's fp32 accumulator (scratch).
+ *   H % ulysses_degree == 0; d 64 or 128; scale <= 0 selects 1/sqrt(d).
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_DEGREE (a degree < 1, their product > 65535,
+ *         or a rank outside the grid), ERR_INDIVISIBLE, ERR_DTYPE, ERR_WORKSPACE,
+ *         ERR_ALIAS, ERR_HIP.
+ */
+int cpattn_unified_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int64_t B, int64_t S_local, int64_t H, int64_t d, float scale,
+                       int ring_degree, int ulysses_degree, int ring_rank, int ulysses_rank,
+                       void* workspace, size_t workspace_bytes, int in_dtype, int out_dtype, void* stream);
+
+/* Bytes of workspace cpattn_unified_fwd needs for these sizes (0 for invalid sizes). */
+size_t cpattn_unified_fwd_workspace_bytes(int64_t B, int64_t S_local, int64_t H, int64_t d,
+                                          int ring_degree, int ulysses_degree, int in_dtype, int out_dtype);
+
 /* Static text for a status code (never NULL). */
 const char* cpattn_status_string(int status);
 

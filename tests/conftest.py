@@ -40,3 +40,19 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def pages_example():
+    """The pages' correctness shape (ParaAttention README, unified attention
+    example): fp16 [B=2, H=24, S=4096, D=64] q/k/v and the unsplit oracle
+    attention over all of it (about 10 s of fp64 BLAS, computed once)."""
+    import oracle
+    from tests.gpu_util import log, rand_f16
+    B, H, S, D = 2, 24, 4096, 64
+    qv, q = rand_f16(0, (B, H, S, D))
+    kv, k = rand_f16(1, (B, H, S, D))
+    vv, v = rand_f16(2, (B, H, S, D))
+    log("[info] pages example: computing the unsplit oracle")
+    ro, rl = oracle.attention(qv, kv, vv)
+    return dict(q=q, k=k, v=v, ref_out=ro, ref_lse=rl, S=S)

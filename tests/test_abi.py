@@ -129,3 +129,37 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_HERE", str(tmp_path))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def unified(L, q=FAKE, k=FAKE2, v=FAKE3, out=FAKE4, lse=FAKE5, B=1, S_loc=8, H=4, d=64, R=2, U=2, rr=0, ur=0,
+            ws=NULL, ws_bytes=0, idt=0, odt=0):
+    return L.cpattn_unified_fwd(q, k, v, out, lse, B, S_loc, H, d, 0.0, R, U, rr, ur, ws, ws_bytes, idt, odt, NULL)
+
+
+def test_unified_validation(L):
+    assert unified(L, R=0) == ERR_DEGREE
+    assert unified(L, U=0) == ERR_DEGREE
+    assert unified(L, R=300, U=300) == ERR_DEGREE          # grid larger than a launch dimension allows
+    assert unified(L, rr=2) == ERR_DEGREE
+    assert unified(L, ur=-1) == ERR_DEGREE
+    assert unified(L, H=6, U=4) == ERR_INDIV
+    assert unified(L, d=96) == ERR_SHAPE
+    assert unified(L, idt=7) == ERR_DTYPE
+    assert unified(L, q=NULL, ws=ctypes.c_void_p(0x70000000), ws_bytes=1 << 20) == ERR_NULL
+    assert unified(L) == ERR_WS                               # no workspace
+    need = L.cpattn_unified_fwd_workspace_bytes(1, 8, 4, 64, 2, 2, 0, 0)
+    assert unified(L, ws=ctypes.c_void_p(0x70000000), ws_bytes=need - 1) == ERR_WS
+    assert unified(L, ws=ctypes.c_void_p(0x70000010), ws_bytes=need) == ERR_WS  # alignment
+    assert unified(L, ws=FAKE, ws_bytes=need) == ERR_ALIAS                      # workspace over q
+    assert unified(L, S_loc=0) == OK
+
+
+def test_unified_workspace_bytes(L):
+    f = L.cpattn_unified_fwd_workspace_bytes
+    B, S_loc, H, d, R, U = 2, 1024, 24, 64, 2, 2
+    hq, seg, allk = H // U, U * S_loc, R * U * S_loc
+    q_b, kv_b, acc_b = B * hq * seg * d * 2, B * hq * allk * d * 2, B * hq * seg * d * 4
+    assert f(B, S_loc, H, d, R, U, 2, 2) == q_b + 2 * kv_b + acc_b      # fp16 out: fp32 accumulator
+    assert f(B, S_loc, H, d, R, U, 2, 1) == q_b + 2 * kv_b              # fp32 out doubles as it
+    assert f(B, S_loc, H, d, 1, U, 0, 0) == B * hq * seg * d * 2 * 3    # one segment: no accumulator
+    assert f(B, S_loc, 25, d, R, U, 0, 0) == 0                          # H % U != 0

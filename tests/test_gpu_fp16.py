@@ -101,19 +101,6 @@ def test_lse_merge_fp16_partials():
     assert np.abs(to_np(acc_l) - rl).max() < 2e-6 * max(1.0, np.abs(rl).max())
 
 
-@pytest.fixture(scope="module")
-def pages_example():
-    """The pages' correctness shape: fp16 [B=2, H=24, S=4096, D=64] q/k/v and the
-    unsplit oracle attention over all of it (about 10 s of fp64 BLAS)."""
-    B, H, S, D = 2, 24, 4096, 64
-    qv, q = rand_f16(0, (B, H, S, D))
-    kv, k = rand_f16(1, (B, H, S, D))
-    vv, v = rand_f16(2, (B, H, S, D))
-    log("[info] pages example: computing the unsplit oracle")
-    ro, rl = oracle.attention(qv, kv, vv)
-    return dict(q=q, k=k, v=v, ref_out=ro, ref_lse=rl, S=S)
-
-
 @pytest.mark.parametrize("world_size", [2, 4])
 def test_pages_example_ring_shares(pages_example, world_size):
     """Every rank's share of a ring of `world_size`: its query rows against the
