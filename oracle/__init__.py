@@ -23,6 +23,8 @@ What it computes, plainly and slowly, in float64 numpy:
 * ``ulysses_seq_to_head`` / ``ulysses_head_to_seq`` -- the Ulysses regroup from
   "every head for a slice of tokens" to "every token for a slice of heads" and
   back ("Context parallelism" page, Ulysses Attention section);
+* ``anything_seq_to_head`` / ``anything_head_to_seq`` -- the same regroup with
+  uneven sequence shards and head groups (Ulysses Anything Attention section);
 * ``unified_rank_share`` / ``unified_all_ranks`` -- Unified attention on a
   ring x Ulysses grid: the regroup, the ring over the regrouped segments, and
   the reverse regroup ("Context parallelism" page, Unified Attention section).
@@ -35,8 +37,10 @@ from .merge import lse_merge, empty_partial
 from .ring import ring_attention
 from .permute import ulysses_seq_to_head, ulysses_head_to_seq
 from .unified import unified_rank_share, unified_all_ranks
+from .permute_any import anything_seq_to_head, anything_head_to_seq, even_split
 
 __all__ = [
     "attention", "attention_rows", "lse_merge", "empty_partial", "ring_attention",
     "ulysses_seq_to_head", "ulysses_head_to_seq", "unified_rank_share", "unified_all_ranks",
+    "anything_seq_to_head", "anything_head_to_seq", "even_split",
 ]

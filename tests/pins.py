@@ -428,3 +428,72 @@ def check_unified_share_rows(unified_share, R=2, U=2, seed=60, B=1, S_loc=2, H_p
                             ref = math.fsum(w[j] * v[b, j, h, e] for j in range(S)) / z
                             assert abs(out[b, hh, i, e] - ref) < 1e-12
                         assert abs(lse[b, hh, i] - (m + math.log(z))) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Ulysses Anything (uneven shards and head groups)
+# --------------------------------------------------------------------------
+
+def _encoded_uneven(seq_lens, B, H, d):
+    """Shards whose values encode (token t, b, head h, e) of the whole sequence."""
+    S = sum(seq_lens)
+    t, b, h, e = np.meshgrid(np.arange(S), np.arange(B), np.arange(H), np.arange(d), indexing="ij")
+    full = (((t * B + b) * H + h) * d + e).astype(np.int64)       # [S, B, H, d]
+    full = np.transpose(full, (1, 0, 2, 3))                          # [B, S, H, d]
+    off = np.concatenate([[0], np.cumsum(seq_lens)]).astype(int)
+    return [np.ascontiguousarray(full[:, off[r]:off[r + 1]]) for r in range(len(seq_lens))]
+
+
+def check_anything_provenance(seq_to_head, seq_lens=(5, 4, 4), head_lens=(3, 2, 2), B=2, d=3):
+    """Every element of head group g came from token t, head hoff_g + h' of the
+    whole sequence (pure-Python loops, uneven tokens and heads)."""
+    H = sum(head_lens)
+    S = sum(seq_lens)
+    shards = _encoded_uneven(list(seq_lens), B, H, d)
+    hoff = np.concatenate([[0], np.cumsum(head_lens)]).astype(int)
+    for g in range(len(head_lens)):
+        out = seq_to_head(shards, list(head_lens), g)
+        assert out.shape == (B, head_lens[g], S, d)
+        for b in range(B):
+            for hh in range(head_lens[g]):
+                for t in range(S):
+                    for e in range(d):
+                        val = int(out[b, hh, t, e])
+                        assert val == (((t * B + b) * H + hoff[g] + hh) * d + e)
+
+
+def check_anything_roundtrip(seq_to_head, head_to_seq, seq_lens=(7, 6, 6, 6), head_lens=(2, 2, 1, 1), B=1, d=4):
+    H = sum(head_lens)
+    shards = _encoded_uneven(list(seq_lens), B, H, d)
+    groups = [seq_to_head(shards, list(head_lens), g) for g in range(len(head_lens))]
+    back = head_to_seq(groups, list(seq_lens))
+    for r in range(len(seq_lens)):
+        assert np.array_equal(back[r], shards[r])
+
+
+def check_anything_even_is_ulysses(seq_to_head, ulysses):
+    """Even lengths: the Anything regroup equals the plain Ulysses one."""
+    r = _rng(70)
+    P, B, S_loc, H, d = 3, 2, 4, 6, 5
+    x = r.standard_normal((P, B, S_loc, H, d))
+    for g in range(P):
+        assert np.array_equal(seq_to_head([x[i] for i in range(P)], [H // P] * P, g), ulysses(x, P, g))
+
+
+def check_anything_attention_equals_unsplit(seq_to_head, head_to_seq, attn, seq_lens=(5, 4, 4), head_lens=(2, 1, 1)):
+    """Regroup, attention per head group over the whole sequence, reverse regroup:
+    every rank's tokens get unsplit attention (torch SDPA, fp64)."""
+    r = _rng(71)
+    B, d = 2, 4
+    H, S = sum(head_lens), sum(seq_lens)
+    full = [r.standard_normal((B, S, H, d)) for _ in range(3)]
+    off = np.concatenate([[0], np.cumsum(seq_lens)]).astype(int)
+    shards = [[np.ascontiguousarray(x[:, off[i]:off[i + 1]]) for i in range(len(seq_lens))] for x in full]
+    outs = []
+    for g in range(len(head_lens)):
+        qg, kg, vg = (seq_to_head(s, list(head_lens), g) for s in shards)
+        outs.append(attn(qg, kg, vg)[0])
+    back = head_to_seq(outs, list(seq_lens))
+    ref, _ = _torch_sdpa_bshd(*full)
+    for i in range(len(seq_lens)):
+        assert np.abs(back[i] - ref[:, off[i]:off[i + 1]]).max() < 1e-12

@@ -254,3 +254,25 @@ def test_unified_reverse_regroup_mutant_is_caught():
         return np.roll(out, U, axis=0), np.roll(lse, U, axis=0)
     with pytest.raises(AssertionError):
         pins.check_unified_equals_unsplit(all_ranks, 2, 2)
+
+
+# --- Ulysses Anything: even-split assumptions planted in a copy of the regroup ---
+
+def ma_even_head_offsets(shards, head_lens, group):
+    """Head offset g * (H // P) instead of the prefix sum of the given head counts."""
+    H = shards[0].shape[2]
+    P = len(shards)
+    h0 = group * (H // P)
+    full = np.concatenate([np.asarray(x)[:, :, h0:h0 + head_lens[group], :] for x in shards], axis=1)
+    return np.ascontiguousarray(np.transpose(full, (0, 2, 1, 3)))
+
+
+def ma_shards_reversed(shards, head_lens, group):
+    """Shards concatenated in reverse rank order."""
+    return oracle.anything_seq_to_head(list(reversed(shards)), head_lens, group)
+
+
+@pytest.mark.parametrize("mut", [ma_even_head_offsets, ma_shards_reversed], ids=lambda f: f.__name__)
+def test_anything_mutant_is_caught(mut):
+    with pytest.raises(AssertionError):
+        pins.check_anything_provenance(mut)

@@ -116,3 +116,28 @@ def test_unified_equals_unsplit(R, U):
 
 def test_unified_share_rows_brute_force():
     pins.check_unified_share_rows(oracle.unified_rank_share)
+
+
+def test_anything_provenance():
+    pins.check_anything_provenance(oracle.anything_seq_to_head)
+    pins.check_anything_provenance(oracle.anything_seq_to_head, seq_lens=(2241, 2240), head_lens=(12, 12), B=1, d=1)
+
+
+def test_anything_roundtrip():
+    pins.check_anything_roundtrip(oracle.anything_seq_to_head, oracle.anything_head_to_seq)
+
+
+def test_anything_even_is_ulysses():
+    pins.check_anything_even_is_ulysses(oracle.anything_seq_to_head, oracle.ulysses_seq_to_head)
+
+
+def test_anything_attention_equals_unsplit():
+    pins.check_anything_attention_equals_unsplit(oracle.anything_seq_to_head, oracle.anything_head_to_seq,
+                                                 oracle.attention)
+
+
+def test_even_split_rule():
+    assert oracle.even_split(4481, 2) == [2241, 2240]
+    assert oracle.even_split(4608, 5) == [922, 922, 922, 921, 921]
+    assert oracle.even_split(24, 5) == [5, 5, 5, 5, 4]
+    assert sum(oracle.even_split(17, 17)) == 17 and oracle.even_split(3, 5) == [1, 1, 1, 0, 0]
