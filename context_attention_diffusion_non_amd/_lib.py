@@ -37,6 +37,9 @@ _SIGNATURES = {
                                         ctypes.c_int, _vp]),
     "cpattn_ulysses_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, _i64, _vp]),
+    "cpattn_ulysses_anything_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, ctypes.c_int,
+                                                        ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.c_int,
+                                                        ctypes.c_int, _i64, _vp]),
     "cpattn_unified_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp,
                                            ctypes.c_size_t, ctypes.c_int, ctypes.c_int, _vp]),

@@ -410,3 +410,50 @@ CPATTN_EXPORT int cpattn_unified_fwd(const void* q, const void* k, const void* v
     return ring_launch(ws + p.q_off, ws + p.k_off, ws + p.v_off, out, lse, B, p.hq, p.s_seg, p.s_all, d, scale, R,
                        nullptr, reinterpret_cast<float*>(ws + p.acc_off), in_dtype, out_dtype, s);
 }
+
+CPATTN_EXPORT int cpattn_ulysses_anything_permute(const void* in, void* out, int64_t B, int64_t H, int64_t d,
+                                                  int degree, const int64_t* seq_lens, const int64_t* head_lens,
+                                                  int group, int direction, int64_t elem_bytes, void* stream) {
+    if (degree < 1 || degree > cpattn::kAnyMaxDegree)
+        return fail(CPATTN_ERR_DEGREE, "degree must lie in [1, %d] (got %d)", cpattn::kAnyMaxDegree, degree);
+    if (group < -1 || group >= degree) return fail(CPATTN_ERR_DEGREE, "group %d outside [-1, %d)", group, degree);
+    if (direction != 0 && direction != 1) return fail(CPATTN_ERR_DTYPE, "direction must be 0 or 1 (got %d)", direction);
+    if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+        return fail(CPATTN_ERR_DTYPE, "elem_bytes must be 1, 2, 4 or 8 (got %lld)", (long long)elem_bytes);
+    if (B < 1 || H < 1 || d < 1) return fail(CPATTN_ERR_SHAPE, "invalid permute shape");
+    if (seq_lens == nullptr || head_lens == nullptr) return fail(CPATTN_ERR_NULL, "seq_lens and head_lens are required");
+    int64_t S = 0, hsum = 0;
+    for (int i = 0; i < degree; ++i) {
+        if (seq_lens[i] < 0 || head_lens[i] < 0)
+            return fail(CPATTN_ERR_CHUNKS, "shard %d: negative length or head count", i);
+        if (seq_lens[i] >= (int64_t(1) << 31) || head_lens[i] >= (int64_t(1) << 31))
+            return fail(CPATTN_ERR_SHAPE, "shard %d too large", i);
+        S += seq_lens[i];
+        hsum += head_lens[i];
+    }
+    if (hsum != H) return fail(CPATTN_ERR_CHUNKS, "head counts sum to %lld, not H=%lld", (long long)hsum, (long long)H);
+    int64_t n = B;
+    if (!mul_ok(n, S) || !mul_ok(n, H) || !mul_ok(n, d) || !mul_ok(n, elem_bytes))
+        return fail(CPATTN_ERR_SHAPE, "permute size overflows");
+    int64_t max_s = 0;
+    for (int i = 0; i < degree; ++i) max_s = seq_lens[i] > max_s ? seq_lens[i] : max_s;
+    int64_t row_bytes = d * elem_bytes, U = 16;
+    while (U > 1 && row_bytes % U != 0) U >>= 1;
+    for (int i = 0; i < degree; ++i) {
+        int64_t units = B;
+        if (!mul_ok(units, max_s) || !mul_ok(units, head_lens[i]) || !mul_ok(units, row_bytes / U) ||
+            units >= (int64_t(1) << 31))
+            return fail(CPATTN_ERR_SHAPE, "one (shard, group) slice exceeds 2^31 copy units");
+    }
+    const size_t seq_bytes = (size_t)n;  // packed shards [B, s_r, H, d]
+    const size_t head_bytes = group < 0 ? (size_t)n : (size_t)(B * head_lens[group] * S * d * elem_bytes);
+    const size_t in_b = direction == 0 ? seq_bytes : head_bytes;
+    const size_t out_b = direction == 0 ? head_bytes : seq_bytes;
+    if (in_b == 0 || out_b == 0) return CPATTN_OK;  // no tokens, or a group without heads: nothing to move
+    if (!in || !out) return fail(CPATTN_ERR_NULL, "in/out is NULL");
+    if (overlaps(in, in_b, out, out_b)) return fail(CPATTN_ERR_ALIAS, "out overlaps in");
+    cpattn::AnyPermuteArgs a{in, out, B, H, d, degree, seq_lens, head_lens, group, direction, elem_bytes};
+    const hipError_t e = cpattn::launch_ulysses_anything_permute(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "permute kernel launch");
+    return CPATTN_OK;
+}

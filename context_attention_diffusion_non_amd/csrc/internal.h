@@ -66,4 +66,21 @@ struct PermuteArgs {
 
 hipError_t launch_ulysses_permute(const PermuteArgs& a, hipStream_t stream);
 
+// Ulysses Anything regroup: uneven sequence shards and head groups.
+constexpr int kAnyMaxDegree = 32;
+
+struct AnyPermuteArgs {
+    const void* in;
+    void* out;
+    int64_t B, H, d;
+    int degree;                              // P
+    const int64_t* seq_lens;                 // host, P entries (tokens of shard r)
+    const int64_t* head_lens;                // host, P entries (heads of group g), sum H
+    int group;                               // -1: all groups (stacked, group g at B * hoff_g * S * d)
+    int direction;                           // 0 seq->head, 1 head->seq
+    int64_t elem_bytes;
+};
+
+hipError_t launch_ulysses_anything_permute(const AnyPermuteArgs& a, hipStream_t stream);
+
 }  // namespace cpattn

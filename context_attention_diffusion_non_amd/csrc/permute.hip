@@ -120,6 +120,80 @@ hipError_t launch_u(const PermuteArgs& a, const PermGeom& g, int ngroups, hipStr
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Ulysses Anything ("Context parallelism" page, Ulysses Anything Attention:
+// neither the sequence nor the heads need divide by the degree).  Shard r
+// holds s_r tokens, packed back to back as [B, s_r, H, d] blocks; group g is
+// h_g consecutive heads:
+//   seq -> head:  out_g[b][h'][off_r + s][:] = shard_r[b][s][hoff_g + h'][:]
+// Grid: x over (b, s, h', unit) of one (shard, group) pair, y = shard, z = group.
+struct AnyGeom {
+    int64_t s_off[kAnyMaxDegree + 1];   // token offsets of the shards (s_off[P] = S)
+    int64_t h_off[kAnyMaxDegree + 1];   // head offsets of the groups (h_off[P] = H)
+    FastDiv f_slen[kAnyMaxDegree];      // tokens per shard (divisor 1 for an empty one)
+    FastDiv f_hlen[kAnyMaxDegree];      // heads per group
+    FastDiv f_upr;                      // units per row
+    int64_t B, H, S, upr;
+    int g0;                             // first group of this call
+    int stacked;                        // output holds every group, group g at B * h_off[g] * S rows
+    int direction;
+};
+
+template <int U, int UNR>
+__global__ __launch_bounds__(NT) void permute_any_kernel(const char* __restrict__ in, char* __restrict__ out,
+                                                         AnyGeom g) {
+    typedef typename Unit<U>::T T;
+    const int r = blockIdx.y;
+    const int grp = g.g0 + (int)blockIdx.z;
+    const uint32_t s_len = (uint32_t)(g.s_off[r + 1] - g.s_off[r]);
+    const uint32_t h_len = (uint32_t)(g.h_off[grp + 1] - g.h_off[grp]);
+    const uint32_t n_units = (uint32_t)g.B * s_len * h_len * (uint32_t)g.upr;
+    const int64_t seq_base = g.B * g.s_off[r] * g.H * g.upr;                  // shard r's block
+    const int64_t head_base = (g.stacked ? g.B * g.h_off[grp] * g.S : 0) * g.upr;  // group grp's block
+
+    T val[UNR];
+    int64_t dst[UNR];
+    bool ok[UNR];
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+        const uint32_t x = ((uint32_t)blockIdx.x * UNR + j) * NT + threadIdx.x;
+        ok[j] = x < n_units;
+        if (!ok[j]) continue;
+        const uint32_t y = fdiv(x, g.f_upr);
+        const uint32_t u = x - y * (uint32_t)g.upr;
+        const uint32_t z = fdiv(y, g.f_hlen[grp]);
+        const uint32_t hh = y - z * h_len;
+        const uint32_t b = fdiv(z, g.f_slen[r]);
+        const uint32_t s = z - b * s_len;
+        const int64_t seq_idx = seq_base + (((int64_t)b * s_len + s) * g.H + g.h_off[grp] + hh) * g.upr + u;
+        const int64_t head_idx = head_base + (((int64_t)b * h_len + hh) * g.S + g.s_off[r] + s) * g.upr + u;
+        const int64_t src = g.direction == 0 ? seq_idx : head_idx;
+        dst[j] = g.direction == 0 ? head_idx : seq_idx;
+        if constexpr (U == 16)
+            val[j] = __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(in) + src));
+        else
+            val[j] = reinterpret_cast<const T*>(in)[src];
+    }
+#pragma unroll
+    for (int j = 0; j < UNR; ++j) {
+        if (!ok[j]) continue;
+        if constexpr (U == 16)
+            __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, val[j]), reinterpret_cast<nt_u32x4*>(out) + dst[j]);
+        else
+            reinterpret_cast<T*>(out)[dst[j]] = val[j];
+    }
+}
+
+template <int U>
+hipError_t launch_any_u(const AnyGeom& g, int P, int ngroups, uint32_t max_units, const void* in, void* out,
+                        hipStream_t stream) {
+    constexpr int UNR = U == 16 ? 1 : 4;
+    const uint32_t nblk = (uint32_t)(((int64_t)max_units + NT * UNR - 1) / (NT * UNR));
+    hipLaunchKernelGGL((permute_any_kernel<U, UNR>), dim3(nblk, (unsigned)P, (unsigned)ngroups), dim3(NT), 0,
+                       stream, static_cast<const char*>(in), static_cast<char*>(out), g);
+    return hipGetLastError();
+}
 }  // namespace
 
 hipError_t launch_ulysses_permute(const PermuteArgs& a, hipStream_t stream) {
@@ -154,6 +228,51 @@ hipError_t launch_ulysses_permute(const PermuteArgs& a, hipStream_t stream) {
         case 4: return launch_u<4>(a, g, ngroups, stream);
         case 2: return launch_u<2>(a, g, ngroups, stream);
         default: return launch_u<1>(a, g, ngroups, stream);
+    }
+}
+
+}  // namespace cpattn
+
+namespace cpattn {
+
+hipError_t launch_ulysses_anything_permute(const AnyPermuteArgs& a, hipStream_t stream) {
+    const int P = a.degree;
+    if (P < 1 || P > kAnyMaxDegree) return hipErrorInvalidValue;
+    const int64_t row_bytes = a.d * a.elem_bytes;
+    int U = 16;
+    while (U > 1 && row_bytes % U != 0) U >>= 1;
+    AnyGeom g{};
+    g.s_off[0] = 0;
+    g.h_off[0] = 0;
+    for (int i = 0; i < P; ++i) {
+        g.s_off[i + 1] = g.s_off[i] + a.seq_lens[i];
+        g.h_off[i + 1] = g.h_off[i] + a.head_lens[i];
+    }
+    g.upr = row_bytes / U;
+    g.B = a.B;
+    g.H = a.H;
+    g.S = g.s_off[P];
+    g.f_upr = make_fastdiv((uint32_t)g.upr);
+    int64_t max_s = 0, max_h = 0;
+    for (int i = 0; i < P; ++i) {
+        g.f_slen[i] = make_fastdiv((uint32_t)(a.seq_lens[i] > 0 ? a.seq_lens[i] : 1));
+        g.f_hlen[i] = make_fastdiv((uint32_t)(a.head_lens[i] > 0 ? a.head_lens[i] : 1));
+        max_s = a.seq_lens[i] > max_s ? a.seq_lens[i] : max_s;
+    }
+    const int ngroups = a.group < 0 ? P : 1;
+    g.g0 = a.group < 0 ? 0 : a.group;
+    for (int i = 0; i < ngroups; ++i) max_h = a.head_lens[g.g0 + i] > max_h ? a.head_lens[g.g0 + i] : max_h;
+    g.stacked = a.group < 0 ? 1 : 0;
+    g.direction = a.direction;
+    const int64_t max_units = a.B * max_s * max_h * g.upr;
+    if (max_units <= 0) return hipSuccess;
+    if (max_units >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    switch (U) {
+        case 16: return launch_any_u<16>(g, P, ngroups, (uint32_t)max_units, a.in, a.out, stream);
+        case 8: return launch_any_u<8>(g, P, ngroups, (uint32_t)max_units, a.in, a.out, stream);
+        case 4: return launch_any_u<4>(g, P, ngroups, (uint32_t)max_units, a.in, a.out, stream);
+        case 2: return launch_any_u<2>(g, P, ngroups, (uint32_t)max_units, a.in, a.out, stream);
+        default: return launch_any_u<1>(g, P, ngroups, (uint32_t)max_units, a.in, a.out, stream);
     }
 }
 

@@ -175,6 +175,55 @@ def ulysses_permute(x: torch.Tensor, degree: int, group: int = 0, direction: int
     return out
 
 
+def even_split(n: int, parts: int):
+    """Default Ulysses Anything split: the first n mod parts pieces one longer."""
+    base, extra = divmod(int(n), int(parts))
+    return [base + (1 if i < extra else 0) for i in range(parts)]
+
+
+def ulysses_anything_permute(x: torch.Tensor, B: int, H: int, d: int, seq_lens: Sequence[int],
+                             head_lens: Optional[Sequence[int]] = None, group: int = 0, direction: int = 0,
+                             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """cpattn_ulysses_anything_permute.
+
+    direction 0: x = the packed sequence shards (shard r = [B, seq_lens[r], H, d] back to back,
+                 B*S*H*d elements) -> [B, head_lens[group], S, d] (group >= 0) or every group
+                 packed back to back as a flat tensor (group == -1).
+    direction 1: the inverse; ``out`` holds the packed shards (created as zeros if not given).
+    head_lens defaults to ``even_split(H, len(seq_lens))``.
+    """
+    _dev(x)
+    P = len(seq_lens)
+    if head_lens is None:
+        head_lens = even_split(H, P)
+    if len(head_lens) != P:
+        raise ValueError("head_lens needs one entry per shard")
+    S = int(sum(seq_lens))
+    seq_numel = B * S * H * d
+    head_numel = seq_numel if group < 0 else B * int(head_lens[group]) * S * d
+    if direction == 0:
+        if x.numel() != seq_numel:
+            raise ValueError(f"x must hold the packed shards ({seq_numel} elements)")
+        if out is None:
+            shape = (B, int(head_lens[group]), S, d) if group >= 0 else (head_numel,)
+            out = torch.empty(shape, dtype=x.dtype, device=x.device)
+        want = head_numel
+    else:
+        if x.numel() != head_numel:
+            raise ValueError(f"x must hold {head_numel} elements")
+        if out is None:
+            out = torch.zeros(seq_numel, dtype=x.dtype, device=x.device)
+        want = seq_numel
+    _dev(out)
+    if out.numel() != want or out.dtype != x.dtype:
+        raise ValueError(f"out must hold {want} elements of x's dtype")
+    sl = (ctypes.c_int64 * P)(*[int(n) for n in seq_lens])
+    hl = (ctypes.c_int64 * P)(*[int(n) for n in head_lens])
+    check(_lib.lib().cpattn_ulysses_anything_permute(_ptr(x), _ptr(out), B, H, d, P, sl, hl, int(group),
+                                                     int(direction), x.element_size(), _stream(x)))
+    return out
+
+
 def unified_fwd_workspace_bytes(B: int, S_local: int, H: int, d: int, ring_degree: int, ulysses_degree: int,
                                 in_dtype: torch.dtype, out_dtype: torch.dtype) -> int:
     return int(_lib.lib().cpattn_unified_fwd_workspace_bytes(B, S_local, H, d, ring_degree, ulysses_degree,
@@ -225,4 +274,5 @@ def unified_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: 
 
 
 __all__ = ["block_fwd", "lse_merge", "ring_fwd", "ring_fwd_workspace_bytes", "ulysses_permute", "unified_fwd",
+           "ulysses_anything_permute", "even_split",
            "unified_fwd_workspace_bytes", "CpattnError", "BF16", "FP16", "FP32"]

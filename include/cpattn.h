@@ -164,6 +164,34 @@ int cpattn_ulysses_permute(const void* in, void* out, int64_t B, int64_t S_local
                            int degree, int group, int direction, int64_t elem_bytes, void* stream);
 
 /*
+ * cpattn_ulysses_anything_permute -- the local half of the Ulysses Anything
+ * all-to-all: sequence shards and head groups of any sizes.
+ *
+ * "Context parallelism" page, Ulysses Anything Attention: plain Ulysses needs
+ * the sequence length and the head count to divide by the degree; this
+ * variant removes both requirements.  Rank r holds seq_lens[r] consecutive
+ * tokens (offset off_r = sum of the earlier lengths) and after the regroup
+ * head_lens[g] consecutive heads (offset hoff_g).
+ *
+ *   direction 0 (sequence -> head):
+ *     in  the P shards packed back to back: shard r is [B, seq_lens[r], H, d]
+ *         at element B * off_r * H * d.
+ *     out [B, head_lens[group], S, d] for head group `group`, S = sum(seq_lens):
+ *         out[b, h', off_r + s, :] = shard_r[b, s, hoff_group + h', :]
+ *         group = -1 writes every group, group g's block at element B * hoff_g * S * d.
+ *   direction 1 (head -> sequence): the inverse map; only the heads of the
+ *     given group(s) are written into the packed shards.
+ *   seq_lens, head_lens: HOST arrays of `degree` counts >= 0; head_lens sum to H.
+ *   degree <= 32; elem_bytes 1, 2, 4 or 8.  The copy is bit-exact.
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_DEGREE (degree outside [1, 32] or group outside
+ *         [-1, P)), ERR_CHUNKS (a negative count, or head counts not summing to H),
+ *         ERR_DTYPE, ERR_ALIAS, ERR_HIP.
+ */
+int cpattn_ulysses_anything_permute(const void* in, void* out, int64_t B, int64_t H, int64_t d, int degree,
+                                    const int64_t* seq_lens, const int64_t* head_lens, int group,
+                                    int direction, int64_t elem_bytes, void* stream);
+
+/*
  * cpattn_unified_fwd -- one rank's share of Unified attention on a
  * ring_degree x ulysses_degree grid of ranks.
  *

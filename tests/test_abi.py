@@ -163,3 +163,24 @@ def test_unified_workspace_bytes(L):
     assert f(B, S_loc, H, d, R, U, 2, 1) == q_b + 2 * kv_b              # fp32 out doubles as it
     assert f(B, S_loc, H, d, 1, U, 0, 0) == B * hq * seg * d * 2 * 3    # one segment: no accumulator
     assert f(B, S_loc, 25, d, R, U, 0, 0) == 0                          # H % U != 0
+
+
+def anyperm(L, inp=FAKE, out=FAKE2, B=1, H=5, d=64, P=2, sl=(3, 2), hl=(3, 2), g=0, direction=0, eb=2):
+    a = None if sl is None else (ctypes.c_int64 * len(sl))(*sl)
+    b = None if hl is None else (ctypes.c_int64 * len(hl))(*hl)
+    return L.cpattn_ulysses_anything_permute(inp, out, B, H, d, P, a, b, g, direction, eb, NULL)
+
+
+def test_anything_permute_validation(L):
+    assert anyperm(L, P=0, sl=(), hl=()) == ERR_DEGREE
+    assert anyperm(L, P=33, sl=(1,) * 33, hl=(1,) * 33, H=33) == ERR_DEGREE
+    assert anyperm(L, g=2) == ERR_DEGREE
+    assert anyperm(L, sl=None) == ERR_NULL
+    assert anyperm(L, hl=(3, 1)) == ERR_CHUNKS          # head counts must sum to H
+    assert anyperm(L, sl=(3, -1)) == ERR_CHUNKS
+    assert anyperm(L, direction=3) == ERR_DTYPE
+    assert anyperm(L, eb=3) == ERR_DTYPE
+    assert anyperm(L, inp=NULL) == ERR_NULL
+    assert anyperm(L, out=ctypes.c_void_p(0x10000 + 128)) == ERR_ALIAS
+    assert anyperm(L, sl=(0, 0)) == OK                    # no tokens: nothing to do
+    assert anyperm(L, out=NULL, H=5, hl=(5, 0), g=1) == OK  # a group without heads: nothing to write
