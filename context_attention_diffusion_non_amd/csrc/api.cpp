@@ -113,6 +113,7 @@ cpattn::AttnArgs make_args(const void* q, const void* k, const void* v, void* ou
     a.lse_out = lse;
     a.acc_in = nullptr;
     a.lse_in = nullptr;
+    a.acc_dtype = cpattn::DT_F32;
     a.n_planes = B * H;
     a.Sq = Sq;
     a.Skv = Skv;
@@ -125,16 +126,19 @@ cpattn::AttnArgs make_args(const void* q, const void* k, const void* v, void* ou
     return a;
 }
 
-// The ring loop after validation: chunk 0 stores its partial into the fp32
-// accumulator (the output itself when it is fp32 or when there is a single
-// chunk, else `acc_ws`), later chunks LSE-merge into it in their epilogue, and
-// the last one writes `out`.  Chunks are `chunk_lens` (NULL: equal lengths).
+// The ring loop after validation: chunk 0 stores its partial into the
+// accumulator, later chunks LSE-merge into it in their epilogue, and the last
+// one writes `out`.  The accumulator is fp32 (convert_to_fp32): the output
+// itself when it is fp32 or when there is a single chunk, else `acc_ws`.  With
+// partials_fp32 false it is `out` in the output dtype, rounded after every
+// merge.  Chunks are `chunk_lens` (NULL: equal lengths).
 int ring_launch(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H, int64_t Sq,
                 int64_t Skv, int64_t d, float scale, int ring_degree, const int64_t* chunk_lens, float* acc_ws,
-                int in_dtype, int out_dtype, hipStream_t s) {
+                int in_dtype, int out_dtype, hipStream_t s, bool partials_fp32 = true) {
     const size_t esz = dtype_bytes(in_dtype);
-    const bool acc_is_out = ring_degree == 1 || out_dtype == CPATTN_FP32;
-    float* acc = acc_is_out ? static_cast<float*>(out) : acc_ws;
+    const bool acc_is_out = ring_degree == 1 || out_dtype == CPATTN_FP32 || !partials_fp32;
+    void* acc = acc_is_out ? out : static_cast<void*>(acc_ws);
+    const int acc_dt = acc_is_out ? out_dtype : (int)cpattn::DT_F32;
     int64_t off = 0;
     for (int c_i = 0; c_i < ring_degree; ++c_i) {
         const int64_t len = chunk_lens ? chunk_lens[c_i] : Skv / ring_degree;
@@ -147,6 +151,7 @@ int ring_launch(const void* q, const void* k, const void* v, void* out, float* l
         } else {
             a.mode = cpattn::EPI_MERGE;
             a.acc_in = acc;
+            a.acc_dtype = acc_dt;
             a.lse_in = lse;
         }
         if (last) {
@@ -154,7 +159,7 @@ int ring_launch(const void* q, const void* k, const void* v, void* out, float* l
             a.out_dtype = out_dtype;
         } else {
             a.out = acc;
-            a.out_dtype = cpattn::DT_F32;
+            a.out_dtype = acc_dt;
         }
         const hipError_t e = cpattn::launch_attn_fwd(a, s);
         if (e != hipSuccess) return hip_fail(e, "attention kernel launch (ring chunk)");
@@ -230,10 +235,12 @@ CPATTN_EXPORT size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64
     return (size_t)n;
 }
 
-CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
-                                  int64_t H, int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree,
-                                  const int64_t* chunk_lens, void* workspace, size_t workspace_bytes, int in_dtype,
-                                  int out_dtype, void* stream) {
+namespace {
+
+int ring_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
+                  int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree, const int64_t* chunk_lens,
+                  bool partials_fp32, void* workspace, size_t workspace_bytes, int in_dtype, int out_dtype,
+                  void* stream) {
     if (ring_degree < 1) return fail(CPATTN_ERR_DEGREE, "ring_degree must be >= 1 (got %d)", ring_degree);
     AttnCheck c;
     int st = check_attn(q, k, v, out, lse, B, H, Sq, Skv, Skv, d, in_dtype, out_dtype, c);
@@ -252,7 +259,7 @@ CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, v
         }
         if (sum != Skv) return fail(CPATTN_ERR_CHUNKS, "chunk lengths do not sum to Skv=%lld", (long long)Skv);
     }
-    const size_t need = cpattn_ring_fwd_workspace_bytes(B, H, Sq, d, ring_degree, out_dtype);
+    const size_t need = partials_fp32 ? cpattn_ring_fwd_workspace_bytes(B, H, Sq, d, ring_degree, out_dtype) : 0;
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < need)
             return fail(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
@@ -268,7 +275,26 @@ CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, v
     if (Sq == 0) return CPATTN_OK;
 
     return ring_launch(q, k, v, out, lse, B, H, Sq, Skv, d, scale, ring_degree, chunk_lens,
-                       static_cast<float*>(workspace), in_dtype, out_dtype, static_cast<hipStream_t>(stream));
+                       static_cast<float*>(workspace), in_dtype, out_dtype, static_cast<hipStream_t>(stream),
+                       partials_fp32);
+}
+
+}  // namespace
+
+CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                  int64_t H, int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree,
+                                  const int64_t* chunk_lens, void* workspace, size_t workspace_bytes, int in_dtype,
+                                  int out_dtype, void* stream) {
+    return ring_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, d, scale, ring_degree, chunk_lens, true, workspace,
+                         workspace_bytes, in_dtype, out_dtype, stream);
+}
+
+CPATTN_EXPORT int cpattn_ring_fwd_cfg(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                                      int64_t H, int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree,
+                                      const int64_t* chunk_lens, int convert_to_fp32, void* workspace,
+                                      size_t workspace_bytes, int in_dtype, int out_dtype, void* stream) {
+    return ring_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, d, scale, ring_degree, chunk_lens, convert_to_fp32 != 0,
+                         workspace, workspace_bytes, in_dtype, out_dtype, stream);
 }
 
 CPATTN_EXPORT int cpattn_ulysses_permute(const void* in, void* out, int64_t B, int64_t S_local, int64_t H, int64_t d,

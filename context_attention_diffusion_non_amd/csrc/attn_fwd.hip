@@ -425,7 +425,7 @@ void attn_fwd_kernel(AttnArgs a) {
     if (!qvalid) return;
 
     float wa = 0.f, wb = inv_l, lnew2 = lse2;
-    const float* acc = nullptr;
+    const char* acc = nullptr;
     if (a.mode == EPI_MERGE) {
         const float la2 = a.lse_in[plane * Sq + qrow] * kLog2e;
         const float mx = fmaxf(la2, lse2);
@@ -442,7 +442,7 @@ void attn_fwd_kernel(AttnArgs a) {
             wb = eb * it * inv_l;
             lnew2 = mx + log2_fast(tot);
         }
-        acc = a.acc_in + (size_t)(plane * Sq + qrow) * D;
+        acc = static_cast<const char*>(a.acc_in) + (size_t)(plane * Sq + qrow) * D * (a.acc_dtype == DT_F32 ? 4 : 2);
     }
 
     const size_t orow = (size_t)(plane * Sq + qrow) * D;
@@ -455,7 +455,14 @@ void attn_fwd_kernel(AttnArgs a) {
             f32x4 x = {o[db][g4 * 4 + 0] * wb, o[db][g4 * 4 + 1] * wb, o[db][g4 * 4 + 2] * wb,
                        o[db][g4 * 4 + 3] * wb};
             if (acc != nullptr && wa != 0.f) {
-                const f32x4 av = *reinterpret_cast<const f32x4*>(acc + db * 32 + g4 * 8 + h * 4);
+                const int e0 = db * 32 + g4 * 8 + h * 4;
+                f32x4 av;
+                if (a.acc_dtype == DT_F32)
+                    av = *reinterpret_cast<const f32x4*>(acc + e0 * 4);
+                else if (a.acc_dtype == DT_F16)
+                    av = __builtin_convertvector(*reinterpret_cast<const f16x4*>(acc + e0 * 2), f32x4);
+                else
+                    av = __builtin_convertvector(*reinterpret_cast<const bf16x4*>(acc + e0 * 2), f32x4);
                 x = x + av * wa;
             }
             r[db * 4 + g4] = x;

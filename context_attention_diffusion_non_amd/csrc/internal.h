@@ -16,7 +16,7 @@ enum ElemType : int {
 // Epilogue of the attention kernel.
 enum AttnEpilogue : int {
     EPI_STORE = 0,  // write the chunk's own (out, lse)
-    EPI_MERGE = 1,  // LSE-merge the chunk's (out, lse) into an fp32 accumulator read from acc_in/lse_in
+    EPI_MERGE = 1,  // LSE-merge the chunk's (out, lse) into the accumulator read from acc_in/lse_in
 };
 
 struct AttnArgs {
@@ -25,7 +25,7 @@ struct AttnArgs {
     const void* v;
     void* out;             // destination of element type out_dtype, [planes, Sq, D]
     float* lse_out;        // [planes, Sq]
-    const float* acc_in;   // EPI_MERGE: fp32 accumulator [planes, Sq, D] (may equal out)
+    const void* acc_in;    // EPI_MERGE: accumulator [planes, Sq, D] of element type acc_dtype (may equal out)
     const float* lse_in;   // EPI_MERGE: accumulator LSE [planes, Sq] (may equal lse_out)
     int64_t n_planes;      // B * H
     int64_t Sq;
@@ -35,6 +35,7 @@ struct AttnArgs {
     int mode;              // AttnEpilogue
     int out_dtype;         // ElemType of out
     int in_dtype;          // ElemType of q/k/v (DT_F32 is rounded to bf16 on staging)
+    int acc_dtype;         // ElemType of acc_in (DT_F32 unless the ring keeps partials in the output dtype)
     int d;                 // 64 or 128
 };
 

@@ -98,9 +98,12 @@ def ring_fwd_workspace_bytes(B: int, H: int, Sq: int, d: int, ring_degree: int, 
 def ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int,
              chunk_lens: Optional[Sequence[int]] = None, *, scale: Optional[float] = None,
              out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-             lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
-             ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """cpattn_ring_fwd: q [B,H,Sq,d] against k/v [B,H,Skv,d] split into ring_degree chunks."""
+             lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             convert_to_fp32: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cpattn_ring_fwd: q [B,H,Sq,d] against k/v [B,H,Skv,d] split into ring_degree chunks.
+
+    convert_to_fp32=False calls cpattn_ring_fwd_cfg and keeps the running output in the
+    output dtype between chunk steps (no workspace)."""
     _dev(q, k, v)
     B, H, Sq, d = q.shape
     skv = k.shape[2]
@@ -117,6 +120,8 @@ def ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int
     if lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
     need = int(_lib.lib().cpattn_ring_fwd_workspace_bytes(B, H, Sq, d, ring_degree, _dtype_code(out)))
+    if not convert_to_fp32:
+        need = 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
@@ -127,9 +132,15 @@ def ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int
         lens = (ctypes.c_int64 * len(chunk_lens))(*[int(x) for x in chunk_lens])
         if len(chunk_lens) != ring_degree:
             raise ValueError("len(chunk_lens) must equal ring_degree")
-    check(_lib.lib().cpattn_ring_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, skv, d,
-                                     _scale(scale), int(ring_degree), lens, _ptr(workspace), ws_bytes,
-                                     _dtype_code(q), _dtype_code(out), _stream(q)))
+    if convert_to_fp32:
+        st = _lib.lib().cpattn_ring_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, skv, d,
+                                        _scale(scale), int(ring_degree), lens, _ptr(workspace), ws_bytes,
+                                        _dtype_code(q), _dtype_code(out), _stream(q))
+    else:
+        st = _lib.lib().cpattn_ring_fwd_cfg(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, skv, d,
+                                            _scale(scale), int(ring_degree), lens, 0, _ptr(workspace), ws_bytes,
+                                            _dtype_code(q), _dtype_code(out), _stream(q))
+    check(st)
     return out, lse
 
 

@@ -140,6 +140,23 @@ int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, floa
                     int in_dtype, int out_dtype, void* stream);
 
 /*
+ * cpattn_ring_fwd_cfg -- cpattn_ring_fwd with ContextParallelConfig's
+ * convert_to_fp32 switch ("Parallelism" API page: convert the output and LSE
+ * to float32 for ring attention numerical stability; default True).
+ *
+ *   convert_to_fp32 != 0: exactly cpattn_ring_fwd (fp32 partials and merges).
+ *   convert_to_fp32 == 0: the running output between chunk steps is kept in
+ *     out_dtype (`out` itself; each merge reads it, merges in fp32 registers and
+ *     rounds back to out_dtype); LSE stays fp32 as the attention step produces
+ *     it.  No workspace is needed.  With out_dtype CPATTN_FP32 both are equal.
+ * Other arguments and errors as cpattn_ring_fwd.
+ */
+int cpattn_ring_fwd_cfg(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t d, float scale,
+                        int ring_degree, const int64_t* chunk_lens, int convert_to_fp32,
+                        void* workspace, size_t workspace_bytes, int in_dtype, int out_dtype, void* stream);
+
+/*
  * cpattn_ulysses_permute -- the local half of the Ulysses all-to-all.
  *
  * "Context parallelism" page, Ulysses Attention: the regroup gives each rank

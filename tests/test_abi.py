@@ -184,3 +184,11 @@ def test_anything_permute_validation(L):
     assert anyperm(L, out=ctypes.c_void_p(0x10000 + 128)) == ERR_ALIAS
     assert anyperm(L, sl=(0, 0)) == OK                    # no tokens: nothing to do
     assert anyperm(L, out=NULL, H=5, hl=(5, 0), g=1) == OK  # a group without heads: nothing to write
+
+
+def test_ring_fwd_cfg_needs_no_workspace_without_fp32(L):
+    f = L.cpattn_ring_fwd_cfg
+    # bf16 out, 2 chunks: the fp32 default needs the accumulator workspace, convert_to_fp32=0 does not
+    assert f(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 2, 16, 16, 128, 0.0, 2, None, 1, NULL, 0, 0, 0, NULL) == ERR_WS
+    assert f(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 2, 0, 16, 128, 0.0, 2, None, 0, NULL, 0, 0, 0, NULL) == OK
+    assert f(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 2, 16, 16, 128, 0.0, 0, None, 0, NULL, 0, 0, 0, NULL) == ERR_DEGREE
