@@ -1,7 +1,7 @@
 // Ulysses sequence <-> head regroup: a strided-to-contiguous row copy.
 //
-// "Context parallelism" page, Ulysses Attention: the all-to-all leaves each
-// rank with every token for a subset of heads; this kernel is the local half of
+// "Context parallelism" page, Ulysses Attention: after the all-to-all a rank
+// holds the whole sequence for its share of the heads; this kernel is the local half of
 // that regroup (and of its inverse), a pure copy of d-element rows:
 //   seq -> head:  out[g'][b][h'][r*S_local + s][:] = in[r][b][s][g*H/P + h'][:]
 //   head -> seq:  the inverse map.

@@ -60,9 +60,9 @@ typedef enum {
  * cpattn_block_fwd -- one chunk step: attention of Q against one K/V block.
  *
  * Defines: out = softmax(Q K^T * scale) V and lse = log sum_j exp(scale * q.k_j)
- * per query row -- the step "each device computes attention between its local
- * Q and KV chunks" of ring_degree in ContextParallelConfig ("Parallelism" API
- * page), with the unmasked, non-causal, dropout-free scaled_dot_product_attention
+ * per query row -- the ring step in which a rank attends its own queries to the
+ * K/V chunk it currently holds (ring_degree in ContextParallelConfig,
+ * "Parallelism" API page), with the unmasked, non-causal, dropout-free scaled_dot_product_attention
  * semantics of the ParaAttention README example.
  *
  *   q    [B, H, Sq, d]  in_dtype, contiguous.
@@ -141,8 +141,8 @@ int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, floa
 
 /*
  * cpattn_ring_fwd_cfg -- cpattn_ring_fwd with ContextParallelConfig's
- * convert_to_fp32 switch ("Parallelism" API page: convert the output and LSE
- * to float32 for ring attention numerical stability; default True).
+ * convert_to_fp32 switch ("Parallelism" API page: output and LSE cast to fp32
+ * to keep the ring numerically stable; on by default).
  *
  *   convert_to_fp32 != 0: exactly cpattn_ring_fwd (fp32 partials and merges).
  *   convert_to_fp32 == 0: the running output between chunk steps is kept in
@@ -159,9 +159,9 @@ int cpattn_ring_fwd_cfg(const void* q, const void* k, const void* v, void* out, 
 /*
  * cpattn_ulysses_permute -- the local half of the Ulysses all-to-all.
  *
- * "Context parallelism" page, Ulysses Attention: the regroup gives each rank
- * every token for a subset of the heads; the second regroup returns results by
- * token.  S and H must divide by the degree P (that page's requirement).
+ * "Context parallelism" page, Ulysses Attention: after the regroup a rank holds
+ * the whole sequence for its share of the heads; the second regroup hands the
+ * results back by token.  S and H must divide by the degree P (that page's requirement).
  *
  *   direction 0 (sequence -> head):
  *     in  [P, B, S_local, H, d]: P sequence shards stacked, shard r holding

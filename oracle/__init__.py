@@ -21,8 +21,8 @@ What it computes, plainly and slowly, in float64 numpy:
   K/V chunk in turn, merged in chunk order ("Context parallelism" page, Ring
   Attention and Ring Anything Attention sections);
 * ``ulysses_seq_to_head`` / ``ulysses_head_to_seq`` -- the Ulysses regroup from
-  "every head for a slice of tokens" to "every token for a slice of heads" and
-  back ("Context parallelism" page, Ulysses Attention section);
+  sequence shards holding all heads to head groups holding the whole sequence,
+  and back ("Context parallelism" page, Ulysses Attention section);
 * ``anything_seq_to_head`` / ``anything_head_to_seq`` -- the same regroup with
   uneven sequence shards and head groups (Ulysses Anything Attention section);
 * ``unified_rank_share`` / ``unified_all_ranks`` -- Unified attention on a

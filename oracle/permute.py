@@ -1,8 +1,8 @@
 """Ulysses sequence<->head regroup as a plain numpy transpose (test infrastructure only).
 
-"Context parallelism" page, Ulysses Attention section: the first all-to-all
-regroups the data so each rank holds every token for a subset of the heads;
-after attention a second all-to-all regroups the results back by token.  The
+"Context parallelism" page, Ulysses Attention section: after the first
+all-to-all a rank holds the whole sequence for its share of the heads; after
+attention a second all-to-all hands the results back by token.  The
 page requires S and H to divide evenly by the degree P.
 
 Layouts (all row-major):
