@@ -5,7 +5,11 @@ FLUX and Ring-Anything shares are compared in full; the Mochi and CogVideoX
 shares on a deterministic query-row sample (all heads; first/last 64 rows,
 both sides of the 128/256 tile boundaries, 256 seeded random rows) that the
 oracle computes row by row.  The CogVideoX permute is compared bit for bit on
-the whole tensors."""
+the whole tensors.  CPATTN_ORACLE_FULL=1 in the environment compares every row
+of the Mochi and CogVideoX shares instead (minutes of fp64 CPU time; raise the
+per-test timeout accordingly)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -34,6 +38,25 @@ def _vals(bits):
     return W.bf16_bits_to_f32(bits).astype(np.float64)
 
 
+FULL = os.environ.get("CPATTN_ORACLE_FULL") == "1"
+
+
+def _rows(n, seed):
+    return np.arange(n) if FULL else W.sample_rows(n, seed=seed)
+
+
+def _oracle_rows(q, k, v, rows, block=2048):
+    """The oracle on the given query rows, a block of rows at a time (bounded memory)."""
+    outs, lses = [], []
+    for i in range(0, len(rows), block):
+        o, l = oracle.attention_rows(q, k, v, rows[i:i + block])
+        outs.append(o)
+        lses.append(l)
+        if FULL:
+            log(f"[info] oracle rows {min(i + block, len(rows))}/{len(rows)}")
+    return np.concatenate(outs, axis=-2), np.concatenate(lses, axis=-1)
+
+
 @pytest.mark.parametrize("name", ["flux", "ring_anything", "mochi"])
 def test_ring_workload(name):
     wl = W.WORKLOADS[name]
@@ -53,8 +76,8 @@ def test_ring_workload(name):
     if wl.q_len * wl.S * wl.H * wl.B <= 24 * 2304 * 4608:
         rows = np.arange(wl.q_len)
     else:
-        rows = W.sample_rows(wl.q_len, seed=wl.seed)
-    ro, rl = oracle.attention_rows(_vals(qb), _vals(kb), _vals(vb), rows)
+        rows = _rows(wl.q_len, wl.seed)
+    ro, rl = _oracle_rows(_vals(qb), _vals(kb), _vals(vb), rows)
     parity(out[:, :, torch.from_numpy(rows).to(out.device)], lse[:, :, torch.from_numpy(rows).to(out.device)],
            ro, rl, f"{name} ring_fwd bf16 ({len(rows)} rows x {wl.B * wl.H} planes)")
 
@@ -76,7 +99,7 @@ def test_cogvideox_ulysses_share():
         got = head[n].view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(got, ref_head[n]), f"permute of {n} not bit-exact"
     log("[parity] cogvideox permute q/k/v: bit-exact")
-    rows = W.sample_rows(wl.S, seed=wl.seed)
-    ro, rl = oracle.attention_rows(_vals(ref_head["q"]), _vals(ref_head["k"]), _vals(ref_head["v"]), rows)
+    rows = _rows(wl.S, wl.seed)
+    ro, rl = _oracle_rows(_vals(ref_head["q"]), _vals(ref_head["k"]), _vals(ref_head["v"]), rows)
     idx = torch.from_numpy(rows).to(out.device)
     parity(out[:, :, idx], lse[:, :, idx], ro, rl, f"cogvideox attention ({len(rows)} rows x {wl.heads_local} heads)")
