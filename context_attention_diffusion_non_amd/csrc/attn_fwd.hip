@@ -9,7 +9,9 @@
 // folded into an fp32 accumulator by the log-sum-exp identity in the epilogue
 // (the convert_to_fp32 ring numerics), so the partial never round-trips HBM.
 //
-// Design (one workgroup = 4 waves = 128 query rows of one plane):
+// Design (one workgroup = NW waves x 32 query rows of one plane; NW = 4, two
+// workgroups per CU, or NW = 8, one per CU, when a launch fits the chip in one
+// round -- the per-row arithmetic is the same either way):
 //   * Everything is computed transposed: S^T = K Q^T and O^T = V^T P^T with
 //     v_mfma_f32_32x32x16_bf16 (or its f16 twin for fp16 inputs, where P is
 //     rounded to fp16 instead of bf16).  In the 32x32 accumulator layout a lane then
@@ -50,24 +52,25 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int BM = 128;  // query rows per workgroup (32 per wave)
 constexpr int BN = 64;   // keys per tile
-constexpr int NT = 256;  // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // log2 units a stale exponent base may lag the true max
 
-template <int D>
+// NW waves per workgroup, 32 query rows each.
+template <int D, int NW>
 struct Cfg {
+    static constexpr int BM = 32 * NW;          // query rows per workgroup
+    static constexpr int NT = 64 * NW;          // threads per workgroup
     static constexpr int RB = D * 2;            // LDS bytes per K or V row (bf16)
     static constexpr int UPR = D / 8;           // 16-byte units per row
     static constexpr int TILE = BN * RB;        // bytes of one K (or V) tile
     static constexpr int LDS = 4 * TILE;        // K stage 0 | K stage 1 | V stage 0 | V stage 1
     static constexpr int CHUNKS = TILE / 1024;  // 1 KB DMA chunks per tile
-    static constexpr int CPW = CHUNKS / 4;      // chunks per wave
+    static constexpr int CPW = CHUNKS / NW;     // chunks per wave
     static constexpr int NK = D / 16;           // k-steps of the S^T product
     static constexpr int NDB = D / 32;          // 32-row blocks of O^T
-    static_assert(CHUNKS % 4 == 0, "tile split over 4 waves");
+    static_assert(CHUNKS % NW == 0, "tile split over the waves");
     static_assert(LDS <= 65536, "stage offsets must fit the 16-bit LDS immediate");
 };
 
@@ -161,12 +164,12 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 // writes lane l's 16 bytes at byte 16 l of the wave's 1 KB chunk, so each lane
 // fetches the global 16 bytes that belong at that swizzled LDS position: unit
 // p = 64 * chunk + l of the tile is row p / UPR, physical unit p % UPR.
-template <int D, bool IS_V>
+template <int D, bool IS_V, int NW>
 struct DmaLane {
-    uint32_t off[Cfg<D>::CPW];  // byte offset of the lane's 16 bytes within the tile's global rows
-    int row[Cfg<D>::CPW];       // tile row of those bytes
+    uint32_t off[Cfg<D, NW>::CPW];  // byte offset of the lane's 16 bytes within the tile's global rows
+    int row[Cfg<D, NW>::CPW];       // tile row of those bytes
     __device__ __forceinline__ void init(int wave, int lane) {
-        using C = Cfg<D>;
+        using C = Cfg<D, NW>;
 #pragma unroll
         for (int i = 0; i < C::CPW; ++i) {
             const int p = (wave * C::CPW + i) * 64 + lane;
@@ -185,10 +188,10 @@ struct DmaLane {
 // path (16-bit elements either way).  fp32 sources are read into registers,
 // rounded to bf16 and stored.  `wave` must be wave-uniform (it
 // selects the LDS chunk, which the DMA takes from M0).
-template <bool F32, int D, bool IS_V>
+template <bool F32, int D, bool IS_V, int NW>
 __device__ __forceinline__ void stage_tile(char* smem, int lds_off, const char* src, int t0, int n,
-                                           const DmaLane<D, IS_V>& dl, int wave, int lane) {
-    using C = Cfg<D>;
+                                           const DmaLane<D, IS_V, NW>& dl, int wave, int lane) {
+    using C = Cfg<D, NW>;
     const char* tile = uniform_ptr(src + (size_t)t0 * (F32 ? 2 * C::RB : C::RB));
     char* dst0 = smem + lds_off + wave * C::CPW * 1024;
     if (t0 + BN <= n) {
@@ -226,10 +229,11 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2], float sl2) {
     return pair_max(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]))) * sl2;
 }
 
-template <int D, int IN>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int IN, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(AttnArgs a) {
-    using C = Cfg<D>;
+    using C = Cfg<D, NW>;
+    constexpr int BM = C::BM;
     constexpr bool F32 = IN == DT_F32;
     typedef typename Op<IN>::T8 op8;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -304,8 +308,8 @@ void attn_fwd_kernel(AttnArgs a) {
             v_lane[db] = row * C::RB + v_unit<D>(row, d0 >> 3) * 16 + (d0 & 7) * 2;
         }
     }
-    DmaLane<D, false> kdl;
-    DmaLane<D, true> vdl;
+    DmaLane<D, false, NW> kdl;
+    DmaLane<D, true, NW> vdl;
     kdl.init(wave, lane);
     vdl.init(wave, lane);
 
@@ -485,12 +489,25 @@ void attn_fwd_kernel(AttnArgs a) {
     if (h == 0) a.lse_out[plane * Sq + qrow] = lnew2 * kLn2;
 }
 
+template <int D, int IN, int NW>
+hipError_t launch_nw(const AttnArgs& a, hipStream_t stream) {
+    using C = Cfg<D, NW>;
+    const int64_t nblk = (a.Sq + C::BM - 1) / C::BM * a.n_planes;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, IN, NW>), dim3((unsigned)nblk), dim3(C::NT), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Four-wave workgroups (two resident per CU) in general; when even those fit
+// the 256-CU chip in one round (512 slots), eight-wave workgroups (one per CU,
+// each K/V tile staged once for 256 queries) run the same per-row arithmetic
+// with half the tile traffic and half the workgroups' fixed costs.
+constexpr int64_t kOneRoundSlots = 512;
+
 template <int D, int IN>
 hipError_t launch_t(const AttnArgs& a, hipStream_t stream) {
-    const int64_t nq = (a.Sq + BM - 1) / BM;
-    const int64_t nblk = nq * a.n_planes;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, IN>), dim3((unsigned)nblk), dim3(NT), 0, stream, a);
-    return hipGetLastError();
+    if ((a.Sq + Cfg<D, 4>::BM - 1) / Cfg<D, 4>::BM * a.n_planes <= kOneRoundSlots)
+        return launch_nw<D, IN, 8>(a, stream);
+    return launch_nw<D, IN, 4>(a, stream);
 }
 
 template <int D>
