@@ -254,6 +254,26 @@ def test_ring_is_deterministic():
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_workgroup_forms_are_bit_identical(d):
+    """The same planes through the eight-wave form (a grid that fits the chip in one round:
+    4 heads x 128 query tiles = 512) and the four-wave form (5 heads, 640 tiles): identical bits,
+    for the store epilogue (block_fwd) and the merge epilogue (ring with uneven chunks)."""
+    log(f"[case] eight-wave vs four-wave workgroups, d={d}")
+    B, H, Sq, Skv = 1, 5, 16384, 300
+    _, q = rand_bf16(91, (B, H, Sq, d))
+    _, k = rand_bf16(92, (B, H, Skv, d))
+    _, v = rand_bf16(93, (B, H, Skv, d))
+    q4, k4, v4 = (t[:, :4].contiguous() for t in (q, k, v))
+    o8, l8 = ops.block_fwd(q4, k4, v4, out_dtype=torch.float32)
+    o4, l4 = ops.block_fwd(q, k, v, out_dtype=torch.float32)
+    r8, rl8 = ops.ring_fwd(q4, k4, v4, 2, [170, 130])
+    r4, rl4 = ops.ring_fwd(q, k, v, 2, [170, 130])
+    torch.cuda.synchronize()
+    assert torch.equal(o8, o4[:, :4]) and torch.equal(l8, l4[:, :4])
+    assert torch.equal(r8.view(torch.int16), r4[:, :4].view(torch.int16)) and torch.equal(rl8, rl4[:, :4])
+
+
 def test_outputs_stay_in_bounds():
     """Outputs carved out of a NaN-filled buffer: every byte outside them is untouched."""
     log("[case] guard bands")
