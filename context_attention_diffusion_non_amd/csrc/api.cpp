@@ -254,8 +254,10 @@ int ring_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
         int64_t sum = 0;
         for (int i = 0; i < ring_degree; ++i) {
             if (chunk_lens[i] < 0) return fail(CPATTN_ERR_CHUNKS, "chunk_lens[%d] = %lld < 0", i, (long long)chunk_lens[i]);
+            // compared before adding, so no sum of lengths can overflow and wrap back to Skv
+            if (chunk_lens[i] > Skv - sum)
+                return fail(CPATTN_ERR_CHUNKS, "chunk lengths exceed Skv=%lld at chunk %d", (long long)Skv, i);
             sum += chunk_lens[i];
-            if (sum > Skv) break;
         }
         if (sum != Skv) return fail(CPATTN_ERR_CHUNKS, "chunk lengths do not sum to Skv=%lld", (long long)Skv);
     }

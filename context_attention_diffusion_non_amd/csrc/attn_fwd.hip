@@ -430,8 +430,11 @@ void attn_fwd_kernel(AttnArgs a) {
 
     float wa = 0.f, wb = inv_l, lnew2 = lse2;
     const char* acc = nullptr;
+    bool acc_empty = true;  // accumulator LSE -inf (bit test: its values are never read then)
     if (a.mode == EPI_MERGE) {
-        const float la2 = a.lse_in[plane * Sq + qrow] * kLog2e;
+        const float la_raw = a.lse_in[plane * Sq + qrow];
+        acc_empty = __float_as_uint(la_raw) == 0xff800000u;
+        const float la2 = la_raw * kLog2e;
         const float mx = fmaxf(la2, lse2);
         if (mx == -INFINITY) {
             wa = 0.f;
@@ -458,7 +461,7 @@ void attn_fwd_kernel(AttnArgs a) {
         for (int g4 = 0; g4 < 4; ++g4) {
             f32x4 x = {o[db][g4 * 4 + 0] * wb, o[db][g4 * 4 + 1] * wb, o[db][g4 * 4 + 2] * wb,
                        o[db][g4 * 4 + 3] * wb};
-            if (acc != nullptr && wa != 0.f) {
+            if (acc != nullptr && !acc_empty) {
                 const int e0 = db * 32 + g4 * 8 + h * 4;
                 f32x4 av;
                 if (a.acc_dtype == DT_F32)

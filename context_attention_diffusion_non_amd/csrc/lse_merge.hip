@@ -26,6 +26,8 @@ constexpr int UNR = 4;  // float4 pieces per thread
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+__device__ __forceinline__ bool is_neg_inf(float x) { return __float_as_uint(x) == 0xff800000u; }
+
 template <int BLK>
 __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a, int64_t n_items, int shift) {
     // shift = log2(d / 4): items per row is a power of two
@@ -68,9 +70,12 @@ __global__ __launch_bounds__(NT) void lse_merge_kernel(MergeArgs a, int64_t n_it
             wb = eb * it;
             lnew = mx + __builtin_amdgcn_logf(tot) * kLn2;
         }
+        // An empty side (LSE = -inf, tested on its bits so the test survives
+        // -fno-honor-nans) is selected out, never multiplied by 0: its values
+        // may be anything, NaN included.
         f32x4 r = {0.f, 0.f, 0.f, 0.f};
-        if (wa != 0.f) r = acc[u] * wa;
-        if (wb != 0.f) r = r + blk[u] * wb;
+        if (!is_neg_inf(la[u])) r = acc[u] * wa;
+        if (!is_neg_inf(lb[u])) r = r + blk[u] * wb;
         __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(a.acc_out + item[u] * 4));
         if ((item[u] & ((1 << shift) - 1)) == 0) a.acc_lse[item[u] >> shift] = lnew;
     }

@@ -31,6 +31,14 @@ def _dev(*ts: torch.Tensor) -> None:
             raise ValueError("cpattn tensors must be contiguous")
 
 
+def _same_kind(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+    """The library reads k and v at q's element size: all three must share dtype and device."""
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError(f"q, k and v must share one dtype (got {q.dtype}, {k.dtype}, {v.dtype})")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError(f"q, k and v must be on one device (got {q.device}, {k.device}, {v.device})")
+
+
 def _stream(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -54,6 +62,7 @@ def block_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, kv_len: Opti
               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, torch.Tensor]:
     """cpattn_block_fwd: attention of q [B,H,Sq,d] against k/v [B,H,kv_ld,d] rows [0, kv_len)."""
+    _same_kind(q, k, v)
     _dev(q, k, v)
     B, H, Sq, d = q.shape
     kv_ld = k.shape[2]
@@ -104,6 +113,7 @@ def ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int
 
     convert_to_fp32=False calls cpattn_ring_fwd_cfg and keeps the running output in the
     output dtype between chunk steps (no workspace)."""
+    _same_kind(q, k, v)
     _dev(q, k, v)
     B, H, Sq, d = q.shape
     skv = k.shape[2]
@@ -252,6 +262,7 @@ def unified_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: 
     Returns out [B, H/U, U*S_local, d] and lse [B, H/U, U*S_local] (head-sharded, before the
     reverse regroup, which is ``ulysses_permute(..., direction=1)`` over a Ulysses group's outputs).
     """
+    _same_kind(q, k, v)
     _dev(q, k, v)
     W, B, S_loc, H, d = q.shape
     _shape(k, q.shape, "k")

@@ -93,6 +93,11 @@ int main(int argc, char** argv) {
         EXPECT(cpattn_ring_fwd(q, k, v, out, lse, 1, 2, 16, 16, 128, 0.f, 3, n.get(), ws, need, CPATTN_BF16,
                                CPATTN_BF16, nullptr),
                CPATTN_ERR_CHUNKS);
+        // lengths whose int64 sum would wrap around to exactly Skv (16)
+        auto w = lens({INT64_MAX, INT64_MAX, 18});
+        EXPECT(cpattn_ring_fwd(q, k, v, out, lse, 1, 2, 16, 16, 128, 0.f, 3, w.get(), ws, need, CPATTN_BF16,
+                               CPATTN_BF16, nullptr),
+               CPATTN_ERR_CHUNKS);
         auto g = lens({6, 5, 5});
         EXPECT(cpattn_ring_fwd(q, k, v, out, lse, 1, 2, 16, 16, 128, 0.f, 3, g.get(), ws, need / 2, CPATTN_BF16,
                                CPATTN_BF16, nullptr),

@@ -73,6 +73,10 @@ def test_ring_fwd_validation(L):
     assert b"not divisible" in L.cpattn_last_error()
     assert ring(L, degree=3, lens=[6, 6, 5], Skv=16) == ERR_CHUNKS
     assert ring(L, degree=3, lens=[6, 11, -1], Skv=16) == ERR_CHUNKS
+    # lengths whose int64 sum wraps around to exactly Skv are rejected, not summed
+    big = (1 << 63) - 1
+    assert ring(L, degree=3, lens=[big, big, 18], Skv=16) == ERR_CHUNKS
+    assert ring(L, degree=3, lens=[16, big, big], Skv=16) == ERR_CHUNKS
     assert ring(L, degree=2, odt=0) == ERR_WS            # bf16 out needs the fp32 accumulator
     need = L.cpattn_ring_fwd_workspace_bytes(1, 2, 16, 128, 2, 0)
     assert need == 1 * 2 * 16 * 128 * 4
@@ -122,6 +126,32 @@ def test_python_binding_refuses_cpu_tensors(lib_path):
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ops.ring_fwd(q, q, q, 1)
+
+
+@pytest.mark.parametrize("fn", ["block_fwd", "ring_fwd", "unified_fwd"])
+def test_python_binding_refuses_mixed_dtypes(fn, monkeypatch):
+    """k/v are read at q's element size, so a dtype mismatch must raise before any library call."""
+    import torch
+    from context_attention_diffusion_non_amd import ops
+
+    def no_call():
+        raise AssertionError("the library was reached")
+    monkeypatch.setattr(_lib, "lib", no_call)
+    if fn == "unified_fwd":
+        q = torch.zeros(2, 1, 4, 2, 64, dtype=torch.float32)
+        kv = torch.zeros(2, 1, 4, 2, 64, dtype=torch.bfloat16)
+        call = lambda a, b, c: ops.unified_fwd(a, b, c, 2, 1, 0, 0)
+    else:
+        q = torch.zeros(1, 1, 4, 64, dtype=torch.float32)
+        kv = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+        call = (lambda a, b, c: ops.block_fwd(a, b, c)) if fn == "block_fwd" else \
+            (lambda a, b, c: ops.ring_fwd(a, b, c, 1))
+    with pytest.raises(TypeError, match="share one dtype"):
+        call(q, kv, kv)
+    with pytest.raises(TypeError, match="share one dtype"):
+        call(q, q, kv)
+    with pytest.raises(TypeError, match="share one dtype"):
+        call(kv, kv, q)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
