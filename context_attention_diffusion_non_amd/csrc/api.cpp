@@ -168,9 +168,121 @@ int ring_launch(const void* q, const void* k, const void* v, void* out, float* l
     return CPATTN_OK;
 }
 
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace of the one-launch ring step for G ranges: the fp32 pieces of split
+// query tiles ([2G, rows, d]), then their LSE ([2G, rows]) at a 256-byte offset.
+size_t ring_slot_bytes(int64_t G, int64_t rows, int64_t d, size_t* lse_off) {
+    const size_t o = align256((size_t)(2 * G * rows * d) * 4);
+    if (lse_off) *lse_off = o;
+    return o + (size_t)(2 * G * rows) * 4;
+}
+
+// Workspace the ring step needs at most for these sizes (any chunking): the
+// one-launch step's slots for its most ranges, or, past kRingMaxChunks
+// chunks, the per-chunk loop's fp32 accumulator when the output is not fp32.
+size_t ring_ws_bound(int64_t B, int64_t H, int64_t Sq, int64_t d, int ring_degree, int out_dtype) {
+    if (ring_degree <= cpattn::kRingMaxChunks) {
+        if (Sq == 0) return 0;
+        const int64_t rows = cpattn::ring_rows(d);
+        return ring_slot_bytes(cpattn::ring_ranges(d), Sq < rows ? Sq : rows, d, nullptr);
+    }
+    if (out_dtype == CPATTN_FP32) return 0;
+    int64_t n = B;
+    if (!mul_ok(n, H) || !mul_ok(n, Sq) || !mul_ok(n, d) || !mul_ok(n, 4)) return 0;
+    return (size_t)n;
+}
+
+// Launch geometry of the one-launch ring step (valid, validated arguments).
+struct RingPlan {
+    cpattn::RingArgs a;
+    size_t need;     // workspace bytes the launch writes (0: no range boundary cuts a query tile)
+    size_t lse_off;
+};
+
+void ring_plan(RingPlan& p, const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
+               int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree, const int64_t* chunk_lens,
+               int in_dtype, int out_dtype) {
+    cpattn::RingArgs& a = p.a;
+    a = cpattn::RingArgs{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse_out = lse;
+    a.n_planes = B * H;
+    a.Sq = Sq;
+    a.kv_plane = Skv * d;
+    a.scale_log2 = resolve_scale(scale, d) * 1.4426950408889634f;
+    a.out_dtype = out_dtype;
+    a.in_dtype = in_dtype;
+    a.d = (int)d;
+    int n = 0, T = 0;
+    int64_t off = 0;
+    for (int i = 0; i < ring_degree; ++i) {
+        const int64_t len = chunk_lens ? chunk_lens[i] : Skv / ring_degree;
+        if (len > 0) {
+            a.chunk_off[n] = (int)off;
+            a.chunk_len[n] = (int)len;
+            a.chunk_tile0[n] = T;
+            T += (int)((len + 63) / 64);
+            ++n;
+        }
+        off += len;
+    }
+    a.chunk_tile0[n] = T;
+    a.n_chunks = n;
+    a.T = T;
+    // Whole query tiles of 256 rows in one round of eight-wave workgroups when even
+    // 128-row tiles would not fill a round of four-wave ones (the chip then stays at
+    // its full clock with some CUs idle, which splitting tiles measured no faster);
+    // else 128-row tiles in rounds, the leftover ones split.
+    const int64_t q4 = a.n_planes * ((Sq + 127) / 128), q8 = a.n_planes * ((Sq + 255) / 256);
+    if (q4 <= cpattn::ring_slots(d, 4) && q8 <= cpattn::ring_slots(d, 8)) {
+        a.nw = 8;
+        a.nq = (int)((Sq + 255) / 256);
+        a.n_ranges = (int)q8;
+        a.rounds = 1;
+        a.left = 0;
+        a.head = 0;
+        a.tail_per = 0;
+        a.tail_rem = 0;
+        a.slot_rows = Sq < 256 ? Sq : 256;
+        p.need = 0;
+        return;
+    }
+    a.nw = 4;
+    const int rows = cpattn::ring_rows(d);
+    a.nq = (int)((Sq + rows - 1) / rows);
+    const int64_t Q = a.n_planes * a.nq;
+    int64_t S = (Q * (int64_t)T + cpattn::kRingMinTiles - 1) / cpattn::kRingMinTiles;
+    if (S > cpattn::ring_ranges(d)) S = cpattn::ring_ranges(d);
+    if (S < 1) S = 1;
+    a.n_ranges = (int)S;
+    a.rounds = (int)(Q / S);
+    a.left = (int)(Q % S);
+    const int64_t L = a.left;
+    int64_t Hd = L > 0 ? (2 * L * T + S) / (2 * S) : 0;  // round(L T / S)
+    if (Hd > T) Hd = T;
+    a.head = (int)Hd;
+    const int64_t tail_units = L * (T - Hd), tail_ranges = S - L;
+    a.tail_per = tail_units / tail_ranges;
+    a.tail_rem = tail_units % tail_ranges;
+    a.slot_rows = Sq < rows ? Sq : rows;
+    // pieces go to the workspace when a leftover tile is cut: heads short of T, or
+    // (no heads) a range boundary inside a tail
+    bool split = L > 0 && Hd > 0 && Hd < T;
+    if (L > 0 && Hd == 0) {
+        for (int64_t t = 1; t < tail_ranges && !split; ++t)
+            split = (t * a.tail_per + (t < a.tail_rem ? t : a.tail_rem)) % T != 0;
+    }
+    p.need = split ? ring_slot_bytes(S, a.slot_rows, d, &p.lse_off) : 0;
+}
+
 }  // namespace
 
-CPATTN_EXPORT int cpattn_version(void) { return 100; }
+CPATTN_EXPORT int cpattn_version(void) { return 110; }
 
 CPATTN_EXPORT const char* cpattn_last_error(void) { return g_last_error; }
 
@@ -228,11 +340,8 @@ CPATTN_EXPORT int cpattn_lse_merge(float* acc_out, float* acc_lse, const void* b
 
 CPATTN_EXPORT size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t d, int ring_degree,
                                                      int out_dtype) {
-    if (B < 1 || H < 1 || Sq < 0 || d < 1 || ring_degree < 1) return 0;
-    if (ring_degree == 1 || out_dtype == CPATTN_FP32) return 0;
-    int64_t n = B;
-    if (!mul_ok(n, H) || !mul_ok(n, Sq) || !mul_ok(n, d) || !mul_ok(n, 4)) return 0;
-    return (size_t)n;
+    if (B < 1 || H < 1 || Sq < 0 || d < 1 || d > 4096 || ring_degree < 1) return 0;
+    return ring_ws_bound(B, H, Sq, d, ring_degree, out_dtype);
 }
 
 namespace {
@@ -261,7 +370,18 @@ int ring_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
         }
         if (sum != Skv) return fail(CPATTN_ERR_CHUNKS, "chunk lengths do not sum to Skv=%lld", (long long)Skv);
     }
-    const size_t need = partials_fp32 ? cpattn_ring_fwd_workspace_bytes(B, H, Sq, d, ring_degree, out_dtype) : 0;
+    // convert_to_fp32 with at most kRingMaxChunks chunks: the whole step in one launch
+    // (plus the merge of split query tiles); otherwise one launch per chunk.
+    // (No keys at all: one launch writes out = 0, lse = -inf, and no workspace is used.)
+    const bool one_launch = partials_fp32 && ring_degree <= cpattn::kRingMaxChunks && Skv > 0;
+    RingPlan plan;
+    size_t need = 0;
+    if (one_launch) {
+        ring_plan(plan, q, k, v, out, lse, B, H, Sq, Skv, d, scale, ring_degree, chunk_lens, in_dtype, out_dtype);
+        need = plan.need;
+    } else if (partials_fp32 && Skv > 0 && ring_degree > 1 && out_dtype != CPATTN_FP32) {
+        need = (size_t)(B * H * Sq * d) * 4;  // the per-chunk loop's fp32 accumulator (sizes checked above)
+    }
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < need)
             return fail(CPATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
@@ -276,6 +396,19 @@ int ring_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
     }
     if (Sq == 0) return CPATTN_OK;
 
+    if (Skv == 0) {
+        const cpattn::AttnArgs a = make_args(q, k, v, out, lse, B, H, Sq, 0, 0, d, scale, in_dtype, out_dtype);
+        const hipError_t e = cpattn::launch_attn_fwd(a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "attention kernel launch (no keys)");
+        return CPATTN_OK;
+    }
+    if (one_launch) {
+        plan.a.part_o = static_cast<float*>(workspace);
+        plan.a.part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.lse_off) : nullptr;
+        const hipError_t e = cpattn::launch_attn_ring(plan.a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "ring step launch");
+        return CPATTN_OK;
+    }
     return ring_launch(q, k, v, out, lse, B, H, Sq, Skv, d, scale, ring_degree, chunk_lens,
                        static_cast<float*>(workspace), in_dtype, out_dtype, static_cast<hipStream_t>(stream),
                        partials_fp32);
@@ -341,7 +474,6 @@ struct UnifiedPlan {
     bool ok;
 };
 
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 UnifiedPlan unified_plan(int64_t B, int64_t S_local, int64_t H, int64_t d, int R, int U, int in_dtype, int out_dtype) {
     UnifiedPlan p{};
@@ -358,12 +490,13 @@ UnifiedPlan unified_plan(int64_t B, int64_t S_local, int64_t H, int64_t d, int R
         !mul_ok(kn, p.hq) || !mul_ok(kn, all) || !mul_ok(kn, d) || !mul_ok(kn, (int64_t)dtype_bytes(in_dtype)) ||
         !mul_ok(an, p.hq) || !mul_ok(an, seg) || !mul_ok(an, d) || !mul_ok(an, 4))
         return p;
-    const bool need_acc = R > 1 && out_dtype != CPATTN_FP32;
+    // the ring step's own workspace (pieces of split query tiles, or the per-chunk fp32 accumulator)
+    const size_t ring_ws = ring_ws_bound(B, p.hq, seg, d, R, out_dtype);
     p.q_off = 0;
     p.k_off = align256((size_t)qn);
     p.v_off = p.k_off + align256((size_t)kn);
     p.acc_off = p.v_off + align256((size_t)kn);
-    p.total = p.acc_off + (need_acc ? align256((size_t)an) : 0);
+    p.total = p.acc_off + align256(ring_ws);
     p.ok = true;
     return p;
 }
@@ -434,6 +567,16 @@ CPATTN_EXPORT int cpattn_unified_fwd(const void* q, const void* k, const void* v
     for (int i = 0; i < 3; ++i) {
         const hipError_t e = cpattn::launch_ulysses_permute(*perms[i], s);
         if (e != hipSuccess) return hip_fail(e, "unified regroup launch");
+    }
+    if (R <= cpattn::kRingMaxChunks) {
+        RingPlan rp;
+        ring_plan(rp, ws + p.q_off, ws + p.k_off, ws + p.v_off, out, lse, B, p.hq, p.s_seg, p.s_all, d, scale, R,
+                  nullptr, in_dtype, out_dtype);
+        rp.a.part_o = reinterpret_cast<float*>(ws + p.acc_off);
+        rp.a.part_lse = reinterpret_cast<float*>(ws + p.acc_off + rp.lse_off);
+        const hipError_t e = cpattn::launch_attn_ring(rp.a, s);
+        if (e != hipSuccess) return hip_fail(e, "unified ring step launch");
+        return CPATTN_OK;
     }
     return ring_launch(ws + p.q_off, ws + p.k_off, ws + p.v_off, out, lse, B, p.hq, p.s_seg, p.s_all, d, scale, R,
                        nullptr, reinterpret_cast<float*>(ws + p.acc_off), in_dtype, out_dtype, s);

@@ -41,6 +41,58 @@ struct AttnArgs {
 
 hipError_t launch_attn_fwd(const AttnArgs& a, hipStream_t stream);
 
+// One ring step in one launch (attn_ring_kernel + ring_fixup_kernel): whole
+// query tiles in rounds of S workgroups, the leftover tiles cut into a head
+// and a tail balanced over all S (see attn_fwd.hip).
+constexpr int kRingMaxChunks = 128;  // non-empty chunks a launch can take
+constexpr int kRingMinTiles = 8;     // fewest key tiles per workgroup
+constexpr int kRingCUs = 256;        // MI355X compute units
+// Waves resident per SIMD (registers and LDS allow 2 at d = 128 and 4 at
+// d = 64), hence workgroups per CU: 8 / NW per SIMD-wave at four waves (NW = 4)
+// or eight (NW = 8), 32 query rows per wave.  Split steps run four-wave
+// workgroups; a step whose whole query tiles fit the chip in one round runs
+// eight-wave ones (256 query rows, each K/V tile staged once for all of them).
+template <int D>
+constexpr int kRingWavesPerSimd = D == 64 ? 4 : 2;
+inline int ring_waves_per_simd(int64_t d) { return d == 64 ? kRingWavesPerSimd<64> : kRingWavesPerSimd<128>; }
+// workgroups of NW waves resident on the chip
+inline int ring_slots(int64_t d, int nw) { return kRingCUs * 4 * ring_waves_per_simd(d) / nw; }
+inline int ring_ranges(int64_t d) { return ring_slots(d, 4); }
+inline int ring_rows(int64_t d) { return 128; }  // query rows per tile of a split step (four waves)
+
+struct RingArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;             // [planes, Sq, D] of out_dtype
+    float* lse_out;        // [planes, Sq]
+    float* part_o;         // workspace: [2 * n_ranges, slot_rows, D] fp32 pieces of cut query tiles
+    float* part_lse;       // workspace: [2 * n_ranges, slot_rows] their LSE, log2 units
+    int64_t n_planes;      // B * H
+    int64_t Sq;
+    int64_t kv_plane;      // elements between consecutive K/V planes (Skv * D)
+    int64_t slot_rows;     // rows per workspace slot: min(query rows per tile, Sq)
+    int64_t tail_per;      // tail units (left * (T - head)) per tail range: tail_per, +1 for the first tail_rem
+    int64_t tail_rem;
+    int T;                 // key tiles per query tile, all chunks
+    int nq;                // query tiles per plane
+    int n_ranges;          // S: workgroups of the launch
+    int rounds;            // R: full rounds of whole query tiles
+    int left;              // L: query tiles after the rounds (< S)
+    int head;              // key tiles of a leftover tile's head (0 .. T)
+    int n_chunks;          // non-empty chunks
+    int nw;                // waves per workgroup: 4, or 8 for a step of whole tiles in one round
+    float scale_log2;
+    int out_dtype;
+    int in_dtype;
+    int d;
+    int chunk_tile0[kRingMaxChunks + 1];  // first key tile of each chunk; [n_chunks] = T
+    int chunk_off[kRingMaxChunks];        // first key row of each chunk
+    int chunk_len[kRingMaxChunks];        // keys of each chunk (> 0)
+};
+
+hipError_t launch_attn_ring(const RingArgs& a, hipStream_t stream);
+
 struct MergeArgs {
     float* acc_out;
     float* acc_lse;

@@ -77,20 +77,38 @@ def test_ring_fwd_validation(L):
     big = (1 << 63) - 1
     assert ring(L, degree=3, lens=[big, big, 18], Skv=16) == ERR_CHUNKS
     assert ring(L, degree=3, lens=[16, big, big], Skv=16) == ERR_CHUNKS
-    assert ring(L, degree=2, odt=0) == ERR_WS            # bf16 out needs the fp32 accumulator
-    need = L.cpattn_ring_fwd_workspace_bytes(1, 2, 16, 128, 2, 0)
-    assert need == 1 * 2 * 16 * 128 * 4
-    assert ring(L, degree=2, odt=0, ws=ctypes.c_void_p(0x50000000), ws_bytes=need - 1) == ERR_WS
-    assert ring(L, degree=2, odt=0, ws=ctypes.c_void_p(0x50000010), ws_bytes=need) == ERR_WS  # alignment
-    assert ring(L, degree=2, odt=0, ws=FAKE4, ws_bytes=need) == ERR_ALIAS                    # ws == out
+    # 513 planes of one 16-row query tile (one more than a round of 512 four-wave workgroups)
+    # against 16 key tiles: one full round, then the leftover tile's 16 tiles split over the
+    # other 511 workgroups (no head: round(16 / 512) = 0), so the step writes pieces:
+    # 2 slots x 512 ranges x 16 rows of d fp32 values, then their LSE.  Any output dtype.
+    for odt in (0, 1, 2):
+        assert ring(L, degree=2, odt=odt, H=513, Skv=1024) == ERR_WS
+    need = 2 * 512 * 16 * 128 * 4 + 2 * 512 * 16 * 4
+    assert L.cpattn_ring_fwd_workspace_bytes(1, 513, 16, 128, 2, 0) == need
+    big_ws = ctypes.c_void_p(0x50000000)
+    assert ring(L, degree=2, H=513, Skv=1024, ws=big_ws, ws_bytes=need - 1) == ERR_WS
+    assert ring(L, degree=2, H=513, Skv=1024, ws=ctypes.c_void_p(0x50000010), ws_bytes=need) == ERR_WS  # alignment
+    assert ring(L, degree=2, H=513, Skv=1024, ws=FAKE4, ws_bytes=need) == ERR_ALIAS                    # ws == out
+    # more chunks than one launch takes: the per-chunk loop and its fp32 accumulator
+    lens = [8] * 130
+    assert ring(L, degree=130, lens=lens, Skv=1040, odt=0) == ERR_WS
 
 
 def test_workspace_bytes(L):
+    """The one-launch ring step's most: two slots per range (512 ranges at d = 128, 1024 at
+    d = 64) of min(128, Sq) rows x d fp32 values, then their LSE at a 256-byte offset --
+    whatever the chunking and output dtype.  Past 128 chunks: the per-chunk loop's fp32
+    accumulator, none for fp32 output."""
     f = L.cpattn_ring_fwd_workspace_bytes
-    assert f(1, 24, 2304, 128, 2, 0) == 24 * 2304 * 128 * 4
-    assert f(1, 24, 2304, 128, 1, 0) == 0        # one chunk writes out directly
-    assert f(1, 24, 2304, 128, 4, 1) == 0        # fp32 out doubles as the accumulator
-    assert f(2, 24, 4096, 64, 2, 2) == 2 * 24 * 4096 * 64 * 4   # fp16 out needs the fp32 accumulator
+    slots = lambda ranges, rows, d: 2 * ranges * rows * d * 4 + 2 * ranges * rows * 4
+    assert f(1, 24, 2304, 128, 2, 0) == slots(512, 128, 128)
+    assert f(1, 24, 2304, 128, 1, 0) == slots(512, 128, 128)
+    assert f(1, 24, 2304, 128, 4, 1) == slots(512, 128, 128)
+    assert f(2, 24, 4096, 64, 2, 2) == slots(1024, 128, 64)
+    assert f(1, 2, 16, 128, 2, 0) == slots(512, 16, 128)
+    assert f(1, 2, 0, 128, 2, 0) == 0
+    assert f(1, 24, 2304, 128, 200, 0) == 24 * 2304 * 128 * 4
+    assert f(1, 24, 2304, 128, 200, 1) == 0
     assert f(0, 24, 2304, 128, 2, 0) == 0
 
 
@@ -188,10 +206,11 @@ def test_unified_workspace_bytes(L):
     f = L.cpattn_unified_fwd_workspace_bytes
     B, S_loc, H, d, R, U = 2, 1024, 24, 64, 2, 2
     hq, seg, allk = H // U, U * S_loc, R * U * S_loc
-    q_b, kv_b, acc_b = B * hq * seg * d * 2, B * hq * allk * d * 2, B * hq * seg * d * 4
-    assert f(B, S_loc, H, d, R, U, 2, 2) == q_b + 2 * kv_b + acc_b      # fp16 out: fp32 accumulator
-    assert f(B, S_loc, H, d, R, U, 2, 1) == q_b + 2 * kv_b              # fp32 out doubles as it
-    assert f(B, S_loc, H, d, 1, U, 0, 0) == B * hq * seg * d * 2 * 3    # one segment: no accumulator
+    q_b, kv_b = B * hq * seg * d * 2, B * hq * allk * d * 2
+    ring_b = 2 * 1024 * 128 * d * 4 + 2 * 1024 * 128 * 4     # the ring step's slots at d = 64
+    assert f(B, S_loc, H, d, R, U, 2, 2) == q_b + 2 * kv_b + ring_b
+    assert f(B, S_loc, H, d, R, U, 2, 1) == q_b + 2 * kv_b + ring_b
+    assert f(B, S_loc, H, d, 1, U, 0, 0) == q_b + 2 * (B * hq * seg * d * 2) + ring_b   # one ring segment
     assert f(B, S_loc, 25, d, R, U, 0, 0) == 0                          # H % U != 0
 
 
@@ -218,7 +237,8 @@ def test_anything_permute_validation(L):
 
 def test_ring_fwd_cfg_needs_no_workspace_without_fp32(L):
     f = L.cpattn_ring_fwd_cfg
-    # bf16 out, 2 chunks: the fp32 default needs the accumulator workspace, convert_to_fp32=0 does not
-    assert f(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 2, 16, 16, 128, 0.0, 2, None, 1, NULL, 0, 0, 0, NULL) == ERR_WS
+    # bf16 out, 2 chunks, split query tiles: the fp32 default needs the pieces' workspace,
+    # convert_to_fp32=0 (one launch per chunk, the output as the running accumulator) does not
+    assert f(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 513, 16, 1024, 128, 0.0, 2, None, 1, NULL, 0, 0, 0, NULL) == ERR_WS
     assert f(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 2, 0, 16, 128, 0.0, 2, None, 0, NULL, 0, 0, 0, NULL) == OK
     assert f(FAKE, FAKE2, FAKE3, FAKE4, FAKE5, 1, 2, 16, 16, 128, 0.0, 0, None, 0, NULL, 0, 0, 0, NULL) == ERR_DEGREE

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from context_attention_diffusion_non_amd import _lib, ops
-from tests.gpu_util import BF16_BARS, FP16_BARS, log, parity, rand_bf16, rand_f16, to_np
+from tests.gpu_util import BF16_BARS, CHUNKED_VS_UNSPLIT, FP16_BARS, log, parity, rand_bf16, rand_f16, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -45,12 +45,20 @@ def test_convert_to_fp32_error_study(study_inputs, n):
     assert res[False]["max_abs_lse"] <= 1e-3
 
 
-def test_convert_to_fp32_fp32_out_is_identical(study_inputs):
+def test_convert_to_fp32_fp32_out_agrees(study_inputs):
+    """With an fp32 output both settings keep the running output in fp32.  The default runs
+    the step in one launch (each chunk's softmax based on the accumulator's LSE), False one
+    launch per chunk (each chunk based on its own maximum), so P is rounded to bf16 against
+    different bases: the two agree to the chunked-vs-unsplit bar, the LSE to fp32 rounding."""
     x = study_inputs
     a = ops.ring_fwd(x["q"], x["k"], x["v"], 4, out_dtype=torch.float32)
     b = ops.ring_fwd(x["q"], x["k"], x["v"], 4, out_dtype=torch.float32, convert_to_fp32=False)
     torch.cuda.synchronize()
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    d_o = (a[0] - b[0]).abs().max().item()
+    d_l = (a[1] - b[1]).abs().max().item()
+    log(f"[parity] fp32 out, convert_to_fp32 True vs False: out={d_o:.3e} lse={d_l:.3e}")
+    assert d_o <= CHUNKED_VS_UNSPLIT and d_l <= 1e-5
+    parity(b[0], b[1], x["ro"], x["rl"], "ring N=4 fp32 out convert_to_fp32=False")
 
 
 @pytest.mark.parametrize("lens", [(0, 64, 0, 100), (129, 127, 65, 3), (1, 1, 1, 1, 60)], ids=str)

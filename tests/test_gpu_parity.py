@@ -150,14 +150,16 @@ def test_ring_uneven_and_empty_chunks(lens, out_dtype):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_ring_chunked_vs_unsplit_and_unfused(d):
-    """GPU chunked (fused merge) vs GPU unsplit, and vs per-chunk block_fwd +
-    standalone lse_merge (the unfused composition), all fp32 out."""
+    """All fp32 out: the ring step against the GPU's unsplit attention, and the per-chunk ring
+    (one launch per chunk, merge fused into the epilogue) against per-chunk block_fwd plus the
+    standalone lse_merge (the unfused composition of the same arithmetic)."""
     log(f"[case] chunked vs unsplit d={d}")
     lens = [300, 301, 299, 100]
     qv, q = rand_bf16(71, (1, 3, 333, d))
     kv, k = rand_bf16(72, (1, 3, sum(lens), d))
     vv, v = rand_bf16(73, (1, 3, sum(lens), d))
     ring_o, ring_l = ops.ring_fwd(q, k, v, 4, lens, out_dtype=torch.float32)
+    per_o, per_l = ops.ring_fwd(q, k, v, 4, lens, out_dtype=torch.float32, convert_to_fp32=False)
     full_o, full_l = ops.block_fwd(q, k, v, out_dtype=torch.float32)
     acc_o = torch.empty_like(ring_o)
     acc_l = torch.full_like(ring_l, -math.inf)
@@ -169,14 +171,19 @@ def test_ring_chunked_vs_unsplit_and_unfused(d):
         ops.lse_merge(acc_o, acc_l, bo, bl)
         off += n
     torch.cuda.synchronize()
-    d1 = (ring_o - full_o).abs().max().item()
     d2 = (ring_l - full_l).abs().max().item()
-    d3 = (ring_o - acc_o).abs().max().item()
-    d4 = (ring_l - acc_l).abs().max().item()
-    log(f"[parity] chunked-vs-unsplit out={d1:.3e} lse={d2:.3e}; fused-vs-unfused out={d3:.3e} lse={d4:.3e}")
-    assert d1 <= CHUNKED_VS_UNSPLIT and d2 <= CHUNKED_VS_UNSPLIT
-    assert d3 <= 1e-5 and d4 <= 1e-5
+    d3 = (per_o - acc_o).abs().max().item()
+    d4 = (per_l - acc_l).abs().max().item()
     ro, rl = oracle.ring_attention(qv, kv, vv, lens)
+    e_ring = float(np.abs(to_np(ring_o) - ro).max())
+    e_full = float(np.abs(to_np(full_o) - ro).max())
+    log(f"[parity] chunked-vs-unsplit lse={d2:.3e}, max|dout| vs oracle chunked {e_ring:.3e} unsplit {e_full:.3e}; "
+        f"fused-vs-unfused out={d3:.3e} lse={d4:.3e}")
+    # 1000 keys: the two outputs differ by the bf16 rounding of P (see test_gpu_ring_step), so the
+    # chunked one is held to the unsplit one's own error against the oracle
+    assert d2 <= CHUNKED_VS_UNSPLIT and e_ring <= 1.5 * e_full + 5e-5
+    assert d3 <= 1e-5 and d4 <= 1e-5
+    parity(ring_o, ring_l, ro, rl, f"ring d={d}")
     parity(acc_o, acc_l, ro, rl, f"unfused ring d={d}")
 
 
@@ -258,7 +265,8 @@ def test_ring_is_deterministic():
 def test_workgroup_forms_are_bit_identical(d):
     """The same planes through the eight-wave form (a grid that fits the chip in one round:
     4 heads x 128 query tiles = 512) and the four-wave form (5 heads, 640 tiles): identical bits,
-    for the store epilogue (block_fwd) and the merge epilogue (ring with uneven chunks)."""
+    for the store epilogue (block_fwd) and the merge epilogue (the per-chunk ring of
+    convert_to_fp32=False, uneven chunks)."""
     log(f"[case] eight-wave vs four-wave workgroups, d={d}")
     B, H, Sq, Skv = 1, 5, 16384, 300
     _, q = rand_bf16(91, (B, H, Sq, d))
@@ -267,8 +275,8 @@ def test_workgroup_forms_are_bit_identical(d):
     q4, k4, v4 = (t[:, :4].contiguous() for t in (q, k, v))
     o8, l8 = ops.block_fwd(q4, k4, v4, out_dtype=torch.float32)
     o4, l4 = ops.block_fwd(q, k, v, out_dtype=torch.float32)
-    r8, rl8 = ops.ring_fwd(q4, k4, v4, 2, [170, 130])
-    r4, rl4 = ops.ring_fwd(q, k, v, 2, [170, 130])
+    r8, rl8 = ops.ring_fwd(q4, k4, v4, 2, [170, 130], convert_to_fp32=False)
+    r4, rl4 = ops.ring_fwd(q, k, v, 2, [170, 130], convert_to_fp32=False)
     torch.cuda.synchronize()
     assert torch.equal(o8, o4[:, :4]) and torch.equal(l8, l4[:, :4])
     assert torch.equal(r8.view(torch.int16), r4[:, :4].view(torch.int16)) and torch.equal(rl8, rl4[:, :4])
