@@ -38,6 +38,10 @@ _SIGNATURES = {
     "cpattn_ring_fwd_cfg": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float,
                                             ctypes.c_int, ctypes.POINTER(_i64), ctypes.c_int, _vp, ctypes.c_size_t,
                                             ctypes.c_int, ctypes.c_int, _vp]),
+    "cpattn_ring_fwd_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                                ctypes.c_float, ctypes.c_int, ctypes.POINTER(_i64), ctypes.c_int,
+                                                ctypes.c_int, _vp]),
+    "cpattn_ring_fwd_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "cpattn_ulysses_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, _i64, _vp]),
     "cpattn_ulysses_anything_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, ctypes.c_int,

@@ -169,14 +169,11 @@ int ring_launch(const void* q, const void* k, const void* v, void* out, float* l
 }
 
 
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t align256(size_t x) { return cpattn::ring_align256(x); }
 
-// Workspace of the one-launch ring step for G ranges: the fp32 pieces of split
-// query tiles ([2G, rows, d]), then their LSE ([2G, rows]) at a 256-byte offset.
 size_t ring_slot_bytes(int64_t G, int64_t rows, int64_t d, size_t* lse_off) {
-    const size_t o = align256((size_t)(2 * G * rows * d) * 4);
-    if (lse_off) *lse_off = o;
-    return o + (size_t)(2 * G * rows) * 4;
+    if (lse_off) *lse_off = cpattn::ring_slot_lse_off(G, rows, d);
+    return cpattn::ring_slot_bytes(G, rows, d);
 }
 
 // Workspace the ring step needs at most for these sizes (any chunking): the
@@ -415,6 +412,22 @@ int ring_fwd_impl(const void* q, const void* k, const void* v, void* out, float*
 }
 
 }  // namespace
+
+namespace cpattn {
+
+int ring_fwd_on_scratch(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
+                        int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree, const int64_t* chunk_lens,
+                        void* scratch, size_t bytes, int in_dtype, int out_dtype, void* stream) {
+    if (ring_degree > kRingMaxChunks)
+        return fail(CPATTN_ERR_DEGREE, "the allocation-free ring step takes at most %d chunks (got %d)", kRingMaxChunks,
+                    ring_degree);
+    return ring_fwd_impl(q, k, v, out, lse, B, H, Sq, Skv, d, scale, ring_degree, chunk_lens, true, scratch, bytes,
+                         in_dtype, out_dtype, stream);
+}
+
+int report_hip_error(hipError_t e, const char* what) { return hip_fail(e, what); }
+
+}  // namespace cpattn
 
 CPATTN_EXPORT int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
                                   int64_t H, int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree,

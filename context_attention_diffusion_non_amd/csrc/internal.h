@@ -60,6 +60,31 @@ inline int ring_slots(int64_t d, int nw) { return kRingCUs * 4 * ring_waves_per_
 inline int ring_ranges(int64_t d) { return ring_slots(d, 4); }
 inline int ring_rows(int64_t d) { return 128; }  // query rows per tile of a split step (four waves)
 
+// Workspace of a split ring step with G ranges: the fp32 pieces of cut query
+// tiles ([2G, rows, d]), then their LSE ([2G, rows]) at a 256-byte offset.
+constexpr size_t ring_align256(size_t x) { return (x + 255) & ~size_t(255); }
+constexpr size_t ring_slot_lse_off(int64_t G, int64_t rows, int64_t d) {
+    return ring_align256((size_t)(2 * G * rows * d) * 4);
+}
+constexpr size_t ring_slot_bytes(int64_t G, int64_t rows, int64_t d) {
+    return ring_slot_lse_off(G, rows, d) + (size_t)(2 * G * rows) * 4;
+}
+// The most any one-launch step needs: 128-row slots for all ranges, either head dim.
+constexpr size_t kRingScratchMax =
+    ring_slot_bytes(kRingCUs * 4 * kRingWavesPerSimd<64> / 4, 128, 64) > ring_slot_bytes(kRingCUs * 4 * kRingWavesPerSimd<128> / 4, 128, 128)
+        ? ring_slot_bytes(kRingCUs * 4 * kRingWavesPerSimd<64> / 4, 128, 64)
+        : ring_slot_bytes(kRingCUs * 4 * kRingWavesPerSimd<128> / 4, 128, 128);
+
+// The ring step (cpattn_ring_fwd's checks and launches) on caller-provided
+// scratch of `bytes` bytes that the library allocated itself, for the
+// allocation-free entry point: more than kRingMaxChunks chunks (whose per-chunk
+// loop needs an accumulator of the problem's size) are refused.
+int ring_fwd_on_scratch(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B, int64_t H,
+                        int64_t Sq, int64_t Skv, int64_t d, float scale, int ring_degree, const int64_t* chunk_lens,
+                        void* scratch, size_t bytes, int in_dtype, int out_dtype, void* stream);
+// Record a failed HIP call as the calling thread's last error; returns CPATTN_ERR_HIP.
+int report_hip_error(hipError_t e, const char* what);
+
 struct RingArgs {
     const void* q;
     const void* k;

@@ -154,6 +154,34 @@ def ring_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int
     return out, lse
 
 
+def ring_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: int,
+                     chunk_lens: Optional[Sequence[int]] = None, *, scale: Optional[float] = None,
+                     out: torch.Tensor, lse: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cpattn_ring_fwd_noalloc: cpattn_ring_fwd on the library's own scratch, no workspace.
+
+    ``out`` and ``lse`` are required (nothing is allocated here either); out's dtype selects
+    the output dtype.  Calls that overlap on one GPU share that scratch and must be serialised."""
+    _same_kind(q, k, v)
+    _dev(q, k, v, out, lse)
+    B, H, Sq, d = q.shape
+    skv = k.shape[2]
+    _shape(k, (B, H, skv, d), "k")
+    _shape(v, (B, H, skv, d), "v")
+    _shape(out, (B, H, Sq, d), "out")
+    _shape(lse, (B, H, Sq), "lse")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    lens = None
+    if chunk_lens is not None:
+        if len(chunk_lens) != ring_degree:
+            raise ValueError("len(chunk_lens) must equal ring_degree")
+        lens = (ctypes.c_int64 * len(chunk_lens))(*[int(x) for x in chunk_lens])
+    check(_lib.lib().cpattn_ring_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, skv, d,
+                                             _scale(scale), int(ring_degree), lens, _dtype_code(q),
+                                             _dtype_code(out), _stream(q)))
+    return out, lse
+
+
 def ulysses_permute(x: torch.Tensor, degree: int, group: int = 0, direction: int = 0,
                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """cpattn_ulysses_permute.
@@ -295,6 +323,7 @@ def unified_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_degree: 
     return out, lse
 
 
-__all__ = ["block_fwd", "lse_merge", "ring_fwd", "ring_fwd_workspace_bytes", "ulysses_permute", "unified_fwd",
+__all__ = ["block_fwd", "lse_merge", "ring_fwd", "ring_fwd_workspace_bytes", "ring_fwd_noalloc", "ulysses_permute",
+           "unified_fwd",
            "ulysses_anything_permute", "even_split",
            "unified_fwd_workspace_bytes", "CpattnError", "BF16", "FP16", "FP32"]

@@ -140,6 +140,36 @@ int cpattn_ring_fwd(const void* q, const void* k, const void* v, void* out, floa
                     int in_dtype, int out_dtype, void* stream);
 
 /*
+ * cpattn_ring_fwd_noalloc -- cpattn_ring_fwd that allocates nothing and takes
+ * no workspace, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The pieces of query tiles cut between workgroups go to a scratch array the
+ * library holds at file scope on every GPU it runs on, for the life of the
+ * process: cpattn_ring_fwd_noalloc_scratch_bytes() bytes (68,157,440), which
+ * cover every shape with up to 128 chunks (the scratch grows with the chip's
+ * workgroup slots, not with B, H or the sequence lengths).  Its device address
+ * is looked up once per device, on the first call there; the call itself makes
+ * no hipMalloc, hipFree or other allocating call.  Nothing in the scratch needs
+ * clearing between calls: every value a call reads was written by that call.
+ * All calls on one GPU share the one array, so calls that overlap on one GPU
+ * (two streams, two threads) race: serialise them.
+ *
+ * Arguments as cpattn_ring_fwd without the workspace; the device is the one
+ * `stream` belongs to (the current device for NULL).  Results are bitwise those
+ * of cpattn_ring_fwd on the same inputs.
+ * Errors: as cpattn_ring_fwd; ERR_DEGREE also for ring_degree > 128 (one launch
+ * per chunk would need an accumulator of the problem's size).
+ */
+int cpattn_ring_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int64_t B, int64_t H, int64_t Sq, int64_t Skv, int64_t d, float scale,
+                            int ring_degree, const int64_t* chunk_lens, int in_dtype, int out_dtype,
+                            void* stream);
+
+/* Bytes of the scratch array cpattn_ring_fwd_noalloc holds on each GPU. */
+size_t cpattn_ring_fwd_noalloc_scratch_bytes(void);
+
+/*
  * cpattn_ring_fwd_cfg -- cpattn_ring_fwd with ContextParallelConfig's
  * convert_to_fp32 switch ("Parallelism" API page: output and LSE cast to fp32
  * to keep the ring numerically stable; on by default).

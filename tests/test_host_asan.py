@@ -25,7 +25,7 @@ def asan_driver(tmp_path_factory):
         pytest.skip("ROCm compilers not available")
     d = tmp_path_factory.mktemp("asan")
     lib = d / "libcpattn_asan.so"
-    srcs = " ".join(os.path.join(CSRC, s) for s in ("attn_fwd.hip", "lse_merge.hip", "permute.hip", "api.cpp"))
+    srcs = " ".join(os.path.join(CSRC, s) for s in ("attn_fwd.hip", "lse_merge.hip", "permute.hip", "api.cpp", "noalloc.hip"))
     build = (f"{HIPCC} --offload-arch=gfx950 -O1 -g -std=c++17 -fPIC -shared "
              f"-Xclang -target-feature -Xclang -packed-fp32-ops -Xarch_device -fno-honor-nans "
              f"-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer "
