@@ -182,8 +182,9 @@ size_t ring_slot_bytes(int64_t G, int64_t rows, int64_t d, size_t* lse_off) {
 size_t ring_ws_bound(int64_t B, int64_t H, int64_t Sq, int64_t d, int ring_degree, int out_dtype) {
     if (ring_degree <= cpattn::kRingMaxChunks) {
         if (Sq == 0) return 0;
-        const int64_t rows = cpattn::ring_rows(d);
-        return ring_slot_bytes(cpattn::ring_ranges(d), Sq < rows ? Sq : rows, d, nullptr);
+        // slots x rows is the same for four- and eight-wave workgroups
+        const int64_t rows = 32 * cpattn::kRingSplitWaves;
+        return ring_slot_bytes(cpattn::ring_slots(d, cpattn::kRingSplitWaves), Sq < rows ? Sq : rows, d, nullptr);
     }
     if (out_dtype == CPATTN_FP32) return 0;
     int64_t n = B;
@@ -234,7 +235,7 @@ void ring_plan(RingPlan& p, const void* q, const void* k, const void* v, void* o
     // Whole query tiles of 256 rows in one round of eight-wave workgroups when even
     // 128-row tiles would not fill a round of four-wave ones (the chip then stays at
     // its full clock with some CUs idle, which splitting tiles measured no faster);
-    // else 128-row tiles in rounds, the leftover ones split.
+    // else query tiles of 32 * kRingSplitWaves rows in rounds, the leftover ones split.
     const int64_t q4 = a.n_planes * ((Sq + 127) / 128), q8 = a.n_planes * ((Sq + 255) / 256);
     if (q4 <= cpattn::ring_slots(d, 4) && q8 <= cpattn::ring_slots(d, 8)) {
         a.nw = 8;
@@ -249,12 +250,12 @@ void ring_plan(RingPlan& p, const void* q, const void* k, const void* v, void* o
         p.need = 0;
         return;
     }
-    a.nw = 4;
-    const int rows = cpattn::ring_rows(d);
+    a.nw = cpattn::kRingSplitWaves;
+    const int rows = 32 * a.nw;
     a.nq = (int)((Sq + rows - 1) / rows);
     const int64_t Q = a.n_planes * a.nq;
     int64_t S = (Q * (int64_t)T + cpattn::kRingMinTiles - 1) / cpattn::kRingMinTiles;
-    if (S > cpattn::ring_ranges(d)) S = cpattn::ring_ranges(d);
+    if (S > cpattn::ring_slots(d, a.nw)) S = cpattn::ring_slots(d, a.nw);
     if (S < 1) S = 1;
     a.n_ranges = (int)S;
     a.rounds = (int)(Q / S);

@@ -98,12 +98,12 @@ int main(int argc, char** argv) {
         EXPECT(cpattn_ring_fwd(q, k, v, out, lse, 1, 2, 16, 16, 128, 0.f, 3, w.get(), ws, need, CPATTN_BF16,
                                CPATTN_BF16, nullptr),
                CPATTN_ERR_CHUNKS);
-        // 513 planes of one 16-row query tile: a round of 512 workgroups, then the leftover
-        // tile's 16 key tiles split over 511 workgroups, so the step writes pieces
-        // (2 slots x 512 ranges x 16 rows x 128 fp32, then 2 x 512 x 16 LSE values)
+        // 513 planes of one 16-row query tile: two rounds of 256 workgroups, then the leftover
+        // tile's 16 key tiles split over 255 workgroups, so the step writes pieces
+        // (2 slots x 256 ranges x 16 rows x 128 fp32, then 2 x 256 x 16 LSE values)
         auto g = lens({512, 256, 256});
         EXPECT(cpattn_ring_fwd(q, k, v, out, lse, 1, 513, 16, 1024, 128, 0.f, 3, g.get(), ws,
-                               2 * 512 * 16 * 128 * 4 + 2 * 512 * 16 * 4 - 1, CPATTN_BF16, CPATTN_BF16, nullptr),
+                               2 * 256 * 16 * 128 * 4 + 2 * 256 * 16 * 4 - 1, CPATTN_BF16, CPATTN_BF16, nullptr),
                CPATTN_ERR_WORKSPACE);
         EXPECT(cpattn_ring_fwd_cfg(q, k, v, out, lse, 1, 2, 16, 16, 128, 0.f, 3, c.get(), 0, nullptr, 0,
                                    CPATTN_BF16, CPATTN_BF16, nullptr),

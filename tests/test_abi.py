@@ -77,13 +77,13 @@ def test_ring_fwd_validation(L):
     big = (1 << 63) - 1
     assert ring(L, degree=3, lens=[big, big, 18], Skv=16) == ERR_CHUNKS
     assert ring(L, degree=3, lens=[16, big, big], Skv=16) == ERR_CHUNKS
-    # 513 planes of one 16-row query tile (one more than a round of 512 four-wave workgroups)
-    # against 16 key tiles: one full round, then the leftover tile's 16 tiles split over the
-    # other 511 workgroups (no head: round(16 / 512) = 0), so the step writes pieces:
-    # 2 slots x 512 ranges x 16 rows of d fp32 values, then their LSE.  Any output dtype.
+    # 513 planes of one 16-row query tile (more than a round of 512 four-wave workgroups) against
+    # 16 key tiles: two rounds of 256 eight-wave workgroups, then the leftover tile's 16 tiles
+    # split over the other 255 (no head: round(16 / 256) = 0), so the step writes pieces:
+    # 2 slots x 256 ranges x 16 rows of d fp32 values, then their LSE.  Any output dtype.
     for odt in (0, 1, 2):
         assert ring(L, degree=2, odt=odt, H=513, Skv=1024) == ERR_WS
-    need = 2 * 512 * 16 * 128 * 4 + 2 * 512 * 16 * 4
+    need = 2 * 256 * 16 * 128 * 4 + 2 * 256 * 16 * 4
     assert L.cpattn_ring_fwd_workspace_bytes(1, 513, 16, 128, 2, 0) == need
     big_ws = ctypes.c_void_p(0x50000000)
     assert ring(L, degree=2, H=513, Skv=1024, ws=big_ws, ws_bytes=need - 1) == ERR_WS
@@ -95,17 +95,17 @@ def test_ring_fwd_validation(L):
 
 
 def test_workspace_bytes(L):
-    """The one-launch ring step's most: two slots per range (512 ranges at d = 128, 1024 at
-    d = 64) of min(128, Sq) rows x d fp32 values, then their LSE at a 256-byte offset --
+    """The one-launch ring step's most: two slots per range (256 eight-wave ranges at d = 128,
+    512 at d = 64) of min(256, Sq) rows x d fp32 values, then their LSE at a 256-byte offset --
     whatever the chunking and output dtype.  Past 128 chunks: the per-chunk loop's fp32
     accumulator, none for fp32 output."""
     f = L.cpattn_ring_fwd_workspace_bytes
     slots = lambda ranges, rows, d: 2 * ranges * rows * d * 4 + 2 * ranges * rows * 4
-    assert f(1, 24, 2304, 128, 2, 0) == slots(512, 128, 128)
-    assert f(1, 24, 2304, 128, 1, 0) == slots(512, 128, 128)
-    assert f(1, 24, 2304, 128, 4, 1) == slots(512, 128, 128)
-    assert f(2, 24, 4096, 64, 2, 2) == slots(1024, 128, 64)
-    assert f(1, 2, 16, 128, 2, 0) == slots(512, 16, 128)
+    assert f(1, 24, 2304, 128, 2, 0) == slots(256, 256, 128)
+    assert f(1, 24, 2304, 128, 1, 0) == slots(256, 256, 128)
+    assert f(1, 24, 2304, 128, 4, 1) == slots(256, 256, 128)
+    assert f(2, 24, 4096, 64, 2, 2) == slots(512, 256, 64)
+    assert f(1, 2, 16, 128, 2, 0) == slots(256, 16, 128)
     assert f(1, 2, 0, 128, 2, 0) == 0
     assert f(1, 24, 2304, 128, 200, 0) == 24 * 2304 * 128 * 4
     assert f(1, 24, 2304, 128, 200, 1) == 0
@@ -207,7 +207,7 @@ def test_unified_workspace_bytes(L):
     B, S_loc, H, d, R, U = 2, 1024, 24, 64, 2, 2
     hq, seg, allk = H // U, U * S_loc, R * U * S_loc
     q_b, kv_b = B * hq * seg * d * 2, B * hq * allk * d * 2
-    ring_b = 2 * 1024 * 128 * d * 4 + 2 * 1024 * 128 * 4     # the ring step's slots at d = 64
+    ring_b = 2 * 512 * 256 * d * 4 + 2 * 512 * 256 * 4       # the ring step's slots at d = 64
     assert f(B, S_loc, H, d, R, U, 2, 2) == q_b + 2 * kv_b + ring_b
     assert f(B, S_loc, H, d, R, U, 2, 1) == q_b + 2 * kv_b + ring_b
     assert f(B, S_loc, H, d, 1, U, 0, 0) == q_b + 2 * (B * hq * seg * d * 2) + ring_b   # one ring segment

@@ -21,7 +21,6 @@ from tests.gpu_util import CHUNKED_VS_UNSPLIT, log, parity, rand_bf16, to_np
 
 pytestmark = pytest.mark.gpu
 
-ROWS = 128      # query rows per tile
 KEYS = 64       # keys per tile
 MIN_TILES = 8   # fewest key tiles per workgroup
 
@@ -29,8 +28,8 @@ MIN_TILES = 8   # fewest key tiles per workgroup
 def pieces(B, H, Sq, d, lens):
     """(T, chunk tile starts, {query tile: [(g0, g1), ...]}) of the one-launch ring step as
     the library plans it.  A step whose 128-row query tiles fit one round of four-wave
-    workgroups runs 256-row tiles whole; otherwise 128-row tiles run whole in rounds of S
-    workgroups and the L leftover tiles are cut at key tile a = round(L T / S) into a head
+    workgroups runs 256-row tiles whole; otherwise 256-row tiles run whole in rounds of S
+    eight-wave workgroups and the L leftover tiles are cut at key tile a = round(L T / S) into a head
     (one workgroup each) and a tail, the tails laid end to end and split into S - L equal
     contiguous ranges."""
     starts, T = [], 0
@@ -42,8 +41,8 @@ def pieces(B, H, Sq, d, lens):
     q4, q8 = B * H * -(-Sq // 128), B * H * -(-Sq // 256)
     if q4 <= slots4 and q8 <= slots8:
         return T, starts, {j: [(0, T)] for j in range(q8)}
-    Q = q4
-    S = min(slots4, max(1, -(-(Q * T) // MIN_TILES)))
+    Q = q8                      # split steps run 256-row tiles too, on the eight-wave slots
+    S = min(slots8, max(1, -(-(Q * T) // MIN_TILES)))
     R, L = divmod(Q, S)
     a = min(T, (2 * L * T + S) // (2 * S)) if L else 0
     out = {j: [(0, T)] for j in range(R * S)}
