@@ -102,9 +102,16 @@ int cpattn_lse_merge(float* acc_out, float* acc_lse, const void* blk_out, const 
                      int64_t rows, int64_t d, int blk_dtype, void* stream);
 
 /*
- * Bytes of workspace cpattn_ring_fwd needs for these sizes: an fp32
- * [B, H, Sq, d] accumulator when ring_degree > 1 and out_dtype is 16-bit, else 0.
- * Returns 0 for invalid sizes as well (cpattn_ring_fwd reports those).
+ * Bytes of workspace that are always enough for cpattn_ring_fwd at these sizes,
+ * whatever the chunk lengths.  Up to 128 chunks the step runs in one launch and
+ * its workspace holds only the pieces of query tiles cut between workgroups:
+ * 2 x S slots of min(256, Sq) rows x d fp32 values, then their LSEs at a 256-byte
+ * offset, S = 256 (d = 128) or 512 (d = 64) -- at most 67,633,152 (d = 128) or
+ * 68,157,440 (d = 64) bytes, independent of B, H and Skv.  Past 128 chunks the
+ * per-chunk fallback needs an fp32 [B, H, Sq, d] accumulator when out_dtype is
+ * 16-bit.  A call may need less (nothing when no query tile is cut); it checks
+ * what its own launch plan writes.  Returns 0 for invalid sizes as well
+ * (cpattn_ring_fwd reports those).
  */
 size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t d, int ring_degree,
                                        int out_dtype);
@@ -127,9 +134,14 @@ size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t
  *   ring_degree >= 1 chunks.  chunk_lens: HOST array of ring_degree lengths, or
  *   NULL for ring_degree equal chunks (then Skv % ring_degree must be 0, the
  *   plain Ring Attention requirement).
- *   workspace: device memory of cpattn_ring_fwd_workspace_bytes(...) bytes,
- *   256-byte aligned (may be NULL when that is 0).  Its contents are scratch.
+ *   workspace: device memory of cpattn_ring_fwd_workspace_bytes(...) bytes (or at
+ *   least what this call's plan writes; NULL when that is 0), 256-byte aligned.
+ *   Its contents are scratch.
  *   d 64 or 128; scale <= 0 selects 1/sqrt(d).
+ * The whole ring loop runs in one launch (plus a small merge launch when query
+ * tiles are cut between workgroups); each chunk's partial is merged into the
+ * fp32 accumulator by LSE rescaling as the chunk ends.  Past 128 chunks the
+ * step runs one launch per chunk.  Results are bitwise repeatable.
  * Result equals attention over all Skv keys up to fp32 rounding of the merges.
  * Errors: ERR_NULL, ERR_SHAPE, ERR_DEGREE, ERR_INDIVISIBLE, ERR_CHUNKS, ERR_DTYPE,
  *         ERR_WORKSPACE, ERR_ALIAS, ERR_HIP.
@@ -178,7 +190,9 @@ size_t cpattn_ring_fwd_noalloc_scratch_bytes(void);
  *   convert_to_fp32 == 0: the running output between chunk steps is kept in
  *     out_dtype (`out` itself; each merge reads it, merges in fp32 registers and
  *     rounds back to out_dtype); LSE stays fp32 as the attention step produces
- *     it.  No workspace is needed.  With out_dtype CPATTN_FP32 both are equal.
+ *     it, one launch per chunk.  No workspace is needed.  With out_dtype
+ *     CPATTN_FP32 both keep fp32 partials and agree to fp32 rounding and to the
+ *     bf16 rounding of the softmax weights against different exponent bases.
  * Other arguments and errors as cpattn_ring_fwd.
  */
 int cpattn_ring_fwd_cfg(const void* q, const void* k, const void* v, void* out, float* lse,
