@@ -624,6 +624,16 @@ __device__ __forceinline__ void ring_piece(const RingArgs& a, char* smem, const 
     int c = 0;
     while (a.chunk_tile0[c + 1] <= g0) ++c;
     int t = g0 - a.chunk_tile0[c];
+    int len = a.chunk_len[c];
+    // the tile after the current one (its chunk's offset and length), known a step ahead so
+    // that the DMA issued after each barrier needs no table load
+    int nc = c, nt = t + 1, noff = a.chunk_off[c], nlen = len;
+    if (nt * BN >= len) {
+        nc = c + 1 < a.n_chunks ? c + 1 : c;
+        nt = 0;
+        noff = a.chunk_off[nc];
+        nlen = a.chunk_len[nc];
+    }
 
     Run<D> st;
     st.reset();
@@ -633,29 +643,30 @@ __device__ __forceinline__ void ring_piece(const RingArgs& a, char* smem, const 
     __syncthreads();
     {
         const size_t co = (size_t)a.chunk_off[c] * D * esz;
-        ln.template stage<F32>(smem, 0, 2 * C::TILE, kp + co, vp + co, t * BN, a.chunk_len[c]);
+        ln.template stage<F32>(smem, 0, 2 * C::TILE, kp + co, vp + co, t * BN, len);
     }
 
     auto step = [&](auto stg_c, int g) __attribute__((always_inline)) {
         constexpr int STG = decltype(stg_c)::value;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        const int len = a.chunk_len[c];
-        const bool chunk_end = (t + 1) * BN >= len;
         if (g + 1 < g1) {
-            const int cn = chunk_end ? c + 1 : c;
-            const int tn = chunk_end ? 0 : t + 1;
-            const size_t co = (size_t)a.chunk_off[cn] * D * esz;
-            ln.template stage<F32>(smem, (1 - STG) * C::TILE, (3 - STG) * C::TILE, kp + co, vp + co, tn * BN,
-                                   a.chunk_len[cn]);
+            const size_t co = (size_t)noff * D * esz;
+            ln.template stage<F32>(smem, (1 - STG) * C::TILE, (3 - STG) * C::TILE, kp + co, vp + co, nt * BN, nlen);
         }
+        const bool chunk_end = (t + 1) * BN >= len;
         tile_math<STG, D, IN, NW>(smem, ln, qf, st, sl2, t * BN, len);
         if (chunk_end || g + 1 == g1) close_chunk<D>(st);
-        if (chunk_end) {
-            ++c;
-            t = 0;
-        } else {
-            ++t;
+        // advance: current <- next, next <- the tile after it
+        c = nc;
+        t = nt;
+        len = nlen;
+        ++nt;
+        if (nt * BN >= nlen) {
+            nc = nc + 1 < a.n_chunks ? nc + 1 : nc;
+            nt = 0;
+            noff = a.chunk_off[nc];
+            nlen = a.chunk_len[nc];
         }
     };
     for (int g = g0; g < g1; g += 2) {
@@ -840,8 +851,13 @@ hipError_t launch_ring_nw(const RingArgs& a, hipStream_t stream) {
 
 template <int D, int IN>
 hipError_t launch_ring_t(const RingArgs& a, hipStream_t stream) {
-    if (a.nw == 8) return launch_ring_nw<D, IN, 8>(a, stream);
-    return launch_ring_nw<D, IN, 4>(a, stream);
+    // the plan picks eight waves for whole-tile steps and kRingSplitWaves for split ones
+    if constexpr (kRingSplitWaves == 8) {
+        return a.nw == 8 ? launch_ring_nw<D, IN, 8>(a, stream) : hipErrorInvalidValue;
+    } else {
+        if (a.nw == 8) return launch_ring_nw<D, IN, 8>(a, stream);
+        return launch_ring_nw<D, IN, kRingSplitWaves>(a, stream);
+    }
 }
 
 template <int D>
