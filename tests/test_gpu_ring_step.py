@@ -146,6 +146,25 @@ def test_more_chunks_than_one_launch_takes():
     parity(out, lse, ro, rl, "130-chunk ring")
 
 
+@pytest.mark.parametrize("B,H,Sq", [(1, 2, 300), (1, 300, 40)], ids=["whole-tiles", "rounds-and-cuts"])
+def test_128_chunks_in_one_launch(B, H, Sq):
+    """128 non-empty chunks of uneven length (1 to 65 keys, so most chunks are one partial key
+    tile): the largest chunk table one launch takes, run whole and in rounds with cut tiles."""
+    lens = [3, 64, 65, 1] * 32
+    T, _, ps = pieces(B, H, Sq, 128, lens)
+    cut = any(p != [(0, T)] for p in ps.values())
+    assert cut == (H == 300)
+    log(f"[case] ring with 128 chunks, B={B} H={H} Sq={Sq} ({'cut tiles' if cut else 'whole tiles'})")
+    skv = sum(lens)
+    qv, q = rand_bf16(9701 + H, (B, H, Sq, 128))
+    kv, k = rand_bf16(9702 + H, (B, H, skv, 128))
+    vv, v = rand_bf16(9703 + H, (B, H, skv, 128))
+    out, lse = ops.ring_fwd(q, k, v, len(lens), lens, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ring_attention(qv, kv, vv, lens)
+    parity(out, lse, ro, rl, f"128-chunk ring H={H}")
+
+
 def test_no_split_needs_no_workspace():
     """A step that runs every query tile whole writes no pieces: no workspace is needed."""
     B, H, Sq, d, lens = 1, 2, 256, 128, (256, 256)
