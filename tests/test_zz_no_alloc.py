@@ -4,8 +4,8 @@ Both run the same kernels and the same launch plan, so the outputs must agree
 bit for bit; here on shapes whose steps cut query tiles (so the library's own
 scratch carries the pieces) and on one that runs whole tiles, two calls in a
 row with the second smaller than the first (the scratch keeps the first call's
-contents, which the second must never read), and on the refusal past 128
-chunks."""
+contents, which the second must never read), under HIP graph capture, and on
+the refusal past 128 chunks."""
 import ctypes
 
 import pytest
@@ -62,6 +62,48 @@ def test_noalloc_whole_tiles(lib_path):
     q, k, v = _inputs(7800, 2, 3, 300, 700, 128)
     ref_o, ref_l, out, lse = _both(q, k, v, (350, 350), torch.bfloat16)
     assert _same(ref_o, out) and torch.equal(ref_l, lse)
+
+
+def test_noalloc_under_graph_capture(lib_path):
+    """The caller it is for: a captured step (pieces of cut tiles in the library's scratch, then
+    the fixup launch) replayed after eager work, bit for bit the eager call each time, also on
+    inputs rewritten in place."""
+    H, Sq, lens, d = 600, 40, (448, 3, 0, 512, 61), 128
+    log(f"[case] noalloc under graph capture: H={H} Sq={Sq} d={d} lens={lens}")
+    q, k, v = _inputs(8100, 1, H, Sq, sum(lens), d)
+    out = torch.empty(1, H, Sq, d, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(1, H, Sq, dtype=torch.float32, device=q.device)
+
+    def call():
+        ops.ring_fwd_noalloc(q, k, v, len(lens), list(lens), out=out, lse=lse)
+
+    call()  # the first call on the device looks the scratch up, outside the capture
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(5.0)
+        lse.fill_(-1.0)
+        ops.ring_fwd(q[:, :7], k[:, :7], v[:, :7], len(lens), list(lens))  # eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same(out, ref_o) and torch.equal(lse, ref_l), f"replay {i} differs from the eager call"
+    q2, k2, v2 = _inputs(8200, 1, H, Sq, sum(lens), d)
+    q.copy_(q2)
+    k.copy_(k2)
+    v.copy_(v2)
+    call()
+    torch.cuda.synchronize()
+    ref2_o, ref2_l = out.clone(), lse.clone()
+    out.zero_()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert _same(out, ref2_o) and torch.equal(lse, ref2_l), "replay on new inputs differs"
 
 
 def test_noalloc_refuses_more_than_128_chunks(lib_path):
